@@ -1,0 +1,148 @@
+"""Oracle of paged decode attention, in float64.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+What is computed ("LLM推理引擎深度实战：从PagedAttention到分布式推理部署", §2.2-§2.3; "大模型推理
+引擎优化：KV Cache 与连续批处理", §2.1-§2.2): in a decode step each sequence's single
+new query token attends over the K/V of all of its tokens.  Those K/V rows sit
+in 16-token physical blocks, and the page table of the sequence maps its
+logical block j to a physical block.  Paging is transparent: the result is
+plain softmax attention over the tokens in logical order.  Per sequence b and
+query head h:
+
+    g        = Hq / Hkv ;  kv head of h = h // g        (reading: consecutive
+                                                          query heads share a
+                                                          KV head)
+    K[t], V[t] = rows (t mod 16) of physical block block_tables[b][t // 16],
+                 kv head h // g, for t = 0 .. L_b - 1
+                 (FP8 cache: code value times that token's scale)
+    s[t]     = scale * <q[b, h], K[t]>
+    w        = exp(s - max s) / sum(exp(s - max s))
+    out[b,h] = sum_t w[t] V[t]            (zeros when L_b == 0)
+
+The gather into contiguous K/V is done first, then the attention, as the
+plain definition reads; numpy matrix products are the only library steps.
+"""
+
+import numpy as np
+
+from .codecs import decode_bits
+
+BLOCK_SIZE = 16
+
+
+def attention_weights(q, K, scale):
+    """Softmax weights of one query over L keys: float64 [L]."""
+    s = scale * (K @ q)
+    e = np.exp(s - np.max(s))
+    return e / np.sum(e)
+
+
+def attend(q, K, V, scale):
+    """Single-query attention over contiguous keys/values (float64).
+
+    q [D], K [L, D], V [L, D] -> [D]; zeros for L == 0.
+    """
+    if K.shape[0] == 0:
+        return np.zeros(V.shape[1], dtype=np.float64)
+    return attention_weights(q, K, scale) @ V
+
+
+def gather_kv(cache, block_table, length, scales=None):
+    """Gather the first ``length`` tokens of one sequence into contiguous rows.
+
+    cache: float64 [num_blocks, 16, Hkv, D] (already decoded); block_table: the
+    sequence's logical->physical block ids; scales: optional float64
+    [num_blocks, 16] per-token multipliers (FP8 cache).  Returns [L, Hkv, D].
+    """
+    rows = []
+    for t in range(length):
+        phys = int(block_table[t // BLOCK_SIZE])
+        off = t % BLOCK_SIZE
+        row = cache[phys, off]
+        if scales is not None:
+            row = row * scales[phys, off]
+        rows.append(row)
+    if not rows:
+        return np.zeros((0,) + cache.shape[2:], dtype=np.float64)
+    return np.stack(rows)
+
+
+def paged_decode(query, key_cache, value_cache, block_tables, context_lens, scale,
+                 q_dtype, cache_dtype, k_scale=None, v_scale=None):
+    """Paged decode attention for a whole batch.
+
+    query: [B, Hq, D] bit patterns (uint16) of ``q_dtype``; caches:
+    [num_blocks, 16, Hkv, D] bit patterns of ``cache_dtype`` ("f16", "bf16",
+    or "fp8_e4m3" with float32 k_scale / v_scale [num_blocks, 16]);
+    block_tables: int [B, max_blocks]; context_lens: int [B].
+    Returns float64 [B, Hq, D].
+    """
+    q = decode_bits(query, q_dtype)
+    kc = decode_bits(key_cache, cache_dtype)
+    vc = decode_bits(value_cache, cache_dtype)
+    ks = None if k_scale is None else np.asarray(k_scale, dtype=np.float64)
+    vs = None if v_scale is None else np.asarray(v_scale, dtype=np.float64)
+    B, Hq, D = q.shape
+    Hkv = kc.shape[2]
+    g = Hq // Hkv
+    out = np.zeros((B, Hq, D), dtype=np.float64)
+    for b in range(B):
+        L = int(context_lens[b])
+        K = gather_kv(kc, block_tables[b], L, ks)
+        V = gather_kv(vc, block_tables[b], L, vs)
+        for h in range(Hq):
+            out[b, h] = attend(q[b, h], K[:, h // g, :], V[:, h // g, :], scale)
+    return out
+
+
+def paged_decode_one(q_vec, key_cache, value_cache, block_table, length, kv_head, scale,
+                     cache_dtype, k_scale=None, v_scale=None):
+    """One (sequence, head) of ``paged_decode``, for sampled checks of large runs.
+
+    q_vec: float64 [D] (already decoded); caches are bit-pattern arrays that
+    need only hold the blocks ``block_table`` names.
+    """
+    kc = decode_bits(key_cache, cache_dtype)
+    vc = decode_bits(value_cache, cache_dtype)
+    ks = None if k_scale is None else np.asarray(k_scale, dtype=np.float64)
+    vs = None if v_scale is None else np.asarray(v_scale, dtype=np.float64)
+    K = gather_kv(kc, block_table, length, ks)
+    V = gather_kv(vc, block_table, length, vs)
+    return attend(np.asarray(q_vec, dtype=np.float64), K[:, kv_head, :], V[:, kv_head, :], scale)
+
+
+def partial_attend(q, K, V, scale):
+    """Unnormalised attention over one partition of the keys.
+
+    Returns (m, l, acc): m = max score, l = sum exp(s - m), acc = sum exp(s - m) V.
+    An empty partition returns (-inf, 0, zeros).
+    """
+    if K.shape[0] == 0:
+        return -np.inf, 0.0, np.zeros(V.shape[1], dtype=np.float64)
+    s = scale * (K @ q)
+    m = np.max(s)
+    e = np.exp(s - m)
+    return m, np.sum(e), e @ V
+
+
+def merge_partials(parts):
+    """Log-sum-exp merge of partition results [(m, l, acc), ...] in list order.
+
+    out = sum_p exp(m_p - M) acc_p / sum_p exp(m_p - M) l_p with M = max_p m_p;
+    zeros when every partition is empty.
+    """
+    ms = np.array([p[0] for p in parts], dtype=np.float64)
+    if len(parts) == 0 or not np.isfinite(ms).any():
+        D = parts[0][2].shape[0] if parts else 0
+        return np.zeros(D, dtype=np.float64)
+    M = np.max(ms)
+    num = 0.0
+    den = 0.0
+    for m, l, acc in parts:
+        if not np.isfinite(m):
+            continue
+        w = np.exp(m - M)
+        num = num + w * acc
+        den = den + w * l
+    return num / den
