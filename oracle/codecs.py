@@ -25,8 +25,8 @@ import numpy as np
 E4M3_MAX = 448.0
 
 
-def decode_f16(bits):
-    """IEEE binary16 bit patterns (uint16 array) -> float64, from the fields."""
+def _f16_fields(bits):
+    """IEEE binary16 bit patterns -> float64, from the sign, exponent and fraction fields."""
     b = np.asarray(bits).astype(np.uint32)
     sign = np.where((b >> 15) & 1, -1.0, 1.0)
     exp = ((b >> 10) & 0x1F).astype(np.int64)
@@ -35,6 +35,15 @@ def decode_f16(bits):
     subnormal = sign * np.ldexp(frac, -24)  # frac * 2^-10 * 2^-14
     special = np.where(frac == 0, sign * np.inf, np.nan)
     return np.where(exp == 0, subnormal, np.where(exp == 31, special, normal))
+
+
+# All 65536 binary16 values, evaluated once from the field definition above.
+_F16_TABLE = _f16_fields(np.arange(1 << 16, dtype=np.uint32))
+
+
+def decode_f16(bits):
+    """IEEE binary16 bit patterns (uint16 array) -> float64 (table of the field definition)."""
+    return _F16_TABLE[np.asarray(bits).astype(np.uint16)]
 
 
 def decode_bf16(bits):

@@ -13,8 +13,9 @@ Sources:
   only for tokens that exist) and §5.3 (FP8 KV cache at per-token granularity).
 
 Slot encoding (a reading; the pages return only a block from the append): a
-slot is ``physical_block * 16 + offset``; a negative slot means "write
-nothing" for that token.
+slot is ``physical_block * 16 + offset``; a slot outside [0, 16 * num_blocks)
+(negative for padding tokens, or past the pool) means "write nothing" for
+that token.
 
 Pools are bit-pattern arrays shaped [num_blocks, 16, num_kv_heads, head_dim]:
 uint16 for float16 / bfloat16 caches and uint8 codes for the FP8 cache, with
@@ -37,8 +38,9 @@ def append_kv(key_cache, value_cache, key, value, slot_mapping):
     """
     kc = np.array(key_cache, copy=True)
     vc = np.array(value_cache, copy=True)
+    num_slots = kc.shape[0] * BLOCK_SIZE
     for t, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
-        if slot < 0:
+        if slot < 0 or slot >= num_slots:
             continue
         blk, off = divmod(int(slot), BLOCK_SIZE)
         kc[blk, off] = key[t]
@@ -86,8 +88,9 @@ def append_kv_e4m3(key_cache, value_cache, k_scale, v_scale, key, value, src_dty
     ksc = np.array(k_scale, copy=True)
     vsc = np.array(v_scale, copy=True)
     row_shape = key_cache.shape[2:]
+    num_slots = key_cache.shape[0] * BLOCK_SIZE
     for t, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
-        if slot < 0:
+        if slot < 0 or slot >= num_slots:
             continue
         blk, off = divmod(int(slot), BLOCK_SIZE)
         kc[blk, off] = kq[t].reshape(row_shape)

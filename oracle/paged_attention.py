@@ -48,24 +48,28 @@ def attend(q, K, V, scale):
     return attention_weights(q, K, scale) @ V
 
 
-def gather_kv(cache, block_table, length, scales=None):
-    """Gather the first ``length`` tokens of one sequence into contiguous rows.
+def gather_kv(cache_bits, block_table, length, dtype, scales=None):
+    """Gather the first ``length`` tokens of one sequence into contiguous float64 rows.
 
-    cache: float64 [num_blocks, 16, Hkv, D] (already decoded); block_table: the
-    sequence's logical->physical block ids; scales: optional float64
-    [num_blocks, 16] per-token multipliers (FP8 cache).  Returns [L, Hkv, D].
+    cache_bits: [num_blocks, 16, Hkv, D] bit patterns of ``dtype``; block_table:
+    the sequence's logical->physical block ids; scales: optional float32
+    [num_blocks, 16] per-token multipliers (FP8 cache).  Token t is row
+    t mod 16 of physical block block_table[t div 16].  Returns [L, Hkv, D].
     """
     rows = []
+    mult = []
     for t in range(length):
         phys = int(block_table[t // BLOCK_SIZE])
         off = t % BLOCK_SIZE
-        row = cache[phys, off]
+        rows.append(cache_bits[phys, off])
         if scales is not None:
-            row = row * scales[phys, off]
-        rows.append(row)
+            mult.append(float(scales[phys, off]))
     if not rows:
-        return np.zeros((0,) + cache.shape[2:], dtype=np.float64)
-    return np.stack(rows)
+        return np.zeros((0,) + tuple(cache_bits.shape[2:]), dtype=np.float64)
+    out = decode_bits(np.stack(rows), dtype)
+    if scales is not None:
+        out = out * np.array(mult, dtype=np.float64)[:, None, None]
+    return out
 
 
 def paged_decode(query, key_cache, value_cache, block_tables, context_lens, scale,
@@ -79,18 +83,14 @@ def paged_decode(query, key_cache, value_cache, block_tables, context_lens, scal
     Returns float64 [B, Hq, D].
     """
     q = decode_bits(query, q_dtype)
-    kc = decode_bits(key_cache, cache_dtype)
-    vc = decode_bits(value_cache, cache_dtype)
-    ks = None if k_scale is None else np.asarray(k_scale, dtype=np.float64)
-    vs = None if v_scale is None else np.asarray(v_scale, dtype=np.float64)
     B, Hq, D = q.shape
-    Hkv = kc.shape[2]
+    Hkv = key_cache.shape[2]
     g = Hq // Hkv
     out = np.zeros((B, Hq, D), dtype=np.float64)
     for b in range(B):
         L = int(context_lens[b])
-        K = gather_kv(kc, block_tables[b], L, ks)
-        V = gather_kv(vc, block_tables[b], L, vs)
+        K = gather_kv(key_cache, block_tables[b], L, cache_dtype, k_scale)
+        V = gather_kv(value_cache, block_tables[b], L, cache_dtype, v_scale)
         for h in range(Hq):
             out[b, h] = attend(q[b, h], K[:, h // g, :], V[:, h // g, :], scale)
     return out
@@ -103,12 +103,8 @@ def paged_decode_one(q_vec, key_cache, value_cache, block_table, length, kv_head
     q_vec: float64 [D] (already decoded); caches are bit-pattern arrays that
     need only hold the blocks ``block_table`` names.
     """
-    kc = decode_bits(key_cache, cache_dtype)
-    vc = decode_bits(value_cache, cache_dtype)
-    ks = None if k_scale is None else np.asarray(k_scale, dtype=np.float64)
-    vs = None if v_scale is None else np.asarray(v_scale, dtype=np.float64)
-    K = gather_kv(kc, block_table, length, ks)
-    V = gather_kv(vc, block_table, length, vs)
+    K = gather_kv(key_cache, block_table, length, cache_dtype, k_scale)
+    V = gather_kv(value_cache, block_table, length, cache_dtype, v_scale)
     return attend(np.asarray(q_vec, dtype=np.float64), K[:, kv_head, :], V[:, kv_head, :], scale)
 
 

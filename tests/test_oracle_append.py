@@ -21,12 +21,12 @@ def test_append_matches_elementwise_loop_and_leaves_other_slots():
     kc, vc = _pools(rng, nb, hkv, d)
     k = rng.integers(0, 1 << 16, size=(T, hkv, d)).astype(np.uint16)
     v = rng.integers(0, 1 << 16, size=(T, hkv, d)).astype(np.uint16)
-    slots = np.array([0, 15, 16, -1, 95, 40, -7], dtype=np.int64)
+    slots = np.array([0, 15, 16, -1, 95, 96, -7], dtype=np.int64)   # 96 = 6 * 16: past the pool
     nk, nv = oracle.append_kv(kc, vc, k, v, slots)
     ek, ev = kc.copy(), vc.copy()
     for t in range(T):
         s = int(slots[t])
-        if s < 0:
+        if s < 0 or s >= nb * BS:
             continue
         for h in range(hkv):
             for e in range(d):
@@ -34,7 +34,7 @@ def test_append_matches_elementwise_loop_and_leaves_other_slots():
                 ev[s // BS, s % BS, h, e] = v[t, h, e]
     assert np.array_equal(nk, ek) and np.array_equal(nv, ev)
     # arguments untouched, untouched slots identical
-    written = {int(s) for s in slots if s >= 0}
+    written = {int(s) for s in slots if 0 <= s < nb * BS}
     for blk in range(nb):
         for off in range(BS):
             if blk * BS + off not in written:
