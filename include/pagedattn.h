@@ -1,0 +1,181 @@
+/*
+ * pagedattn.h - C ABI of the gfx950 (MI355X) paged decode attention library.
+ *
+ * Two operations, both from the pages' description of PagedAttention:
+ *
+ *  - pa_append_kv: write each new token's K and V rows into the slot of the
+ *    KV cache that the block manager gave it ("大模型推理引擎优化：KV Cache 与连续批处理",
+ *    §2.1 and §2.2: every decode step adds the new token's K/V, in 16-token
+ *    blocks handed out on demand), optionally quantising them to FP8 E4M3
+ *    with one float32 scale per token ("LLM推理引擎深度实战：从PagedAttention到分布式推理部署",
+ *    §5.3: FP8 KV cache, per-token granularity).
+ *
+ *  - pa_decode: one query token per sequence attends over that sequence's
+ *    cached K/V, which sit in fixed 16-token physical blocks reached through
+ *    the sequence's page table; the kernel turns logical token indices into
+ *    physical addresses, so the result is plain softmax attention over the
+ *    tokens in logical order ("LLM推理引擎深度实战：…", §2.2 and §2.3).
+ *
+ * Layouts (all row-major, contiguous, little-endian):
+ *   query        [num_seqs, num_heads, head_dim]                 q_dtype
+ *   out          [num_seqs, num_heads, head_dim]                 q_dtype
+ *   key_cache    [num_blocks, 16, num_kv_heads, head_dim]        cache_dtype
+ *   value_cache  [num_blocks, 16, num_kv_heads, head_dim]        cache_dtype
+ *   k_scale      [num_blocks, 16] float32   (FP8 cache only; one scale per token slot)
+ *   v_scale      [num_blocks, 16] float32   (FP8 cache only)
+ *   block_tables [num_seqs, max_blocks_per_seq] int32: physical block of
+ *                logical block j of sequence b
+ *   context_lens [num_seqs] int32: tokens of sequence b, including the one
+ *                appended in this step
+ *   slot_mapping [num_tokens] int64: physical_block * 16 + offset; < 0 = skip
+ *
+ * Query head h reads KV head h / (num_heads / num_kv_heads) (consecutive
+ * query heads share a KV head).  Block size is fixed at 16 tokens.
+ *
+ * Ownership and ordering: every pointer argument is a caller-owned device
+ * buffer (except where noted); the library allocates nothing, keeps nothing
+ * after a call returns and has no mutable global state, so it may be called
+ * from several threads.  Work is enqueued asynchronously on `stream` (a
+ * hipStream_t; NULL = the null stream); an append followed by a decode on
+ * the same stream is ordered.  Host-side argument checks run before anything
+ * is enqueued and never read device memory, so no call synchronises.
+ *
+ * Errors: functions return a pa_status.  PA_ERR_* codes other than
+ * PA_ERR_HIP come from host-side checks and leave every buffer untouched.
+ * PA_ERR_HIP reports a launch failure (hipGetLastError after the launch).
+ * Device contents are the caller's contract: slots and table entries that
+ * fall outside [0, num_blocks) are ignored by the kernels (that token or block
+ * is skipped, never read or written), and context_lens are clamped to
+ * [0, min(max_context_len, 16 * max_blocks_per_seq)].
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_BLOCK_SIZE 16
+
+typedef enum pa_status {
+    PA_OK = 0,
+    PA_ERR_NULL = 1,        /* a required pointer is NULL                        */
+    PA_ERR_SHAPE = 2,       /* a size is out of range or inconsistent            */
+    PA_ERR_DTYPE = 3,       /* unsupported dtype or dtype combination            */
+    PA_ERR_UNSUPPORTED = 4, /* head_dim or head grouping the kernels do not cover */
+    PA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required        */
+    PA_ERR_HIP = 6,         /* the HIP runtime reported an error                 */
+    PA_ERR_ALIGN = 7        /* a buffer is not 16-byte aligned                   */
+} pa_status;
+
+typedef enum pa_dtype {
+    PA_F16 = 0,       /* IEEE binary16                                  */
+    PA_BF16 = 1,      /* bfloat16                                       */
+    PA_FP8_E4M3 = 2,  /* OCP FP8 E4M3 (fn): bias 7, max 448, no Inf      */
+    PA_F32 = 3        /* listed for completeness; no operation takes it */
+} pa_dtype;
+
+/*
+ * pa_append_kv - slot-mapped KV append (reshape_and_cache).
+ *
+ * For each token t < num_tokens with s = slot_mapping[t] in
+ * [0, 16 * num_blocks): block = s / 16, offset = s % 16, and
+ *   key_cache[block, offset, :, :]   <- key[t, :, :]
+ *   value_cache[block, offset, :, :] <- value[t, :, :]
+ * Tokens with s outside that range are skipped.
+ *
+ * key, value: [num_tokens, num_kv_heads, head_dim] of src_dtype.
+ * cache_dtype == src_dtype (PA_F16 or PA_BF16): a bit-exact copy; k_scale and
+ *   v_scale are ignored (may be NULL).
+ * cache_dtype == PA_FP8_E4M3 (src PA_F16 or PA_BF16): K and V of each token
+ *   are quantised separately over all num_kv_heads*head_dim elements:
+ *   amax = max|x| (float32), scale = amax / 448 (IEEE float32 division;
+ *   1.0 when amax == 0), code = E4M3(x / scale) with the division in float32,
+ *   round-to-nearest-even and saturation to +-448; the codes go to the cache
+ *   and the scales to k_scale[block, offset] / v_scale[block, offset].
+ *
+ * Two tokens with the same slot in one call race (undefined which wins).
+ * head_dim must be 64 or 128.  All buffers 16-byte aligned (scales 4-byte).
+ */
+pa_status pa_append_kv(const void *key, const void *value,
+                       void *key_cache, void *value_cache,
+                       float *k_scale, float *v_scale,
+                       const int64_t *slot_mapping,
+                       int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                       int64_t num_blocks,
+                       int32_t src_dtype, int32_t cache_dtype,
+                       void *stream);
+
+/*
+ * pa_decode_partition_size - the partition (split-K chunk) length, in tokens,
+ * that pa_decode uses for these arguments: `partition_size` itself when it is
+ * non-zero, otherwise the library's choice for this batch shape.  Returns 0
+ * when the arguments are invalid (partition_size not a positive multiple of
+ * 16 and not 0, or a non-positive size).
+ */
+int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_context_len,
+                                 int32_t partition_size);
+
+/*
+ * pa_decode_workspace_bytes - device workspace pa_decode needs for these
+ * arguments (0 when a single partition covers max_context_len, so no
+ * cross-partition reduction is needed; (size_t)-1 for invalid arguments).
+ * Layout: float32 partial sums [num_seqs, num_heads, P, head_dim] followed by
+ * float32 (max, sum) pairs [num_seqs, num_heads, P, 2], where
+ * P = ceil(max_context_len / partition length).
+ */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_context_len,
+                                 int32_t partition_size);
+
+/*
+ * pa_decode - paged decode attention, one query token per sequence.
+ *
+ * For each sequence b with L = context_lens[b] (clamped as above) and each
+ * query head h, with g = num_heads / num_kv_heads and kv = h / g:
+ *   K[t], V[t] = row (t % 16) of physical block block_tables[b, t / 16], KV
+ *                head kv, for t < L (FP8 cache: code value * k_scale / v_scale
+ *                of that slot)
+ *   out[b, h, :] = sum_t softmax_t(scale * <query[b, h, :], K[t]>) V[t, :]
+ * computed with float32 accumulation and rounded to q_dtype (round to nearest
+ * even).  L == 0 gives a zero row.  Only slots t < L are read: whatever the
+ * other slots and the table entries past ceil(L/16) hold never reaches out.
+ *
+ * Sequences longer than one partition are split into partitions of
+ * pa_decode_partition_size(...) tokens whose partial results (running max,
+ * sum of exponentials, weighted V sum) go to `workspace` and are merged in
+ * ascending partition order, so for fixed inputs and partition size the
+ * output is bitwise deterministic.
+ *
+ * Supported (q_dtype, cache_dtype): (F16, F16), (BF16, BF16), (F16, FP8_E4M3),
+ * (BF16, FP8_E4M3).  head_dim 64 or 128.  num_heads a multiple of
+ * num_kv_heads.  k_scale / v_scale required for FP8, ignored otherwise.
+ * max_context_len: a host-side upper bound of context_lens, used to size the
+ * partition grid.  workspace: device buffer of at least
+ * pa_decode_workspace_bytes(...) bytes (may be NULL when that is 0); out must
+ * not alias any input.
+ */
+pa_status pa_decode(void *out, const void *query,
+                    const void *key_cache, const void *value_cache,
+                    const float *k_scale, const float *v_scale,
+                    const int32_t *block_tables, const int32_t *context_lens,
+                    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                    int32_t head_dim, int64_t num_blocks,
+                    int32_t max_blocks_per_seq, int32_t max_context_len,
+                    float scale, int32_t partition_size,
+                    int32_t q_dtype, int32_t cache_dtype,
+                    void *workspace, size_t workspace_bytes,
+                    void *stream);
+
+/* pa_status_string - static, human-readable name of a status code. */
+const char *pa_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

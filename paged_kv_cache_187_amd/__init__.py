@@ -1,0 +1,20 @@
+"""gfx950 (MI355X) paged decode attention and slot-mapped KV append.
+
+The work runs in hand-written HIP kernels behind the C ABI declared in
+``include/pagedattn.h`` (``libpagedattn.so``, built in-tree by
+``paged_kv_cache_187_amd.build``); this package only marshals torch tensors
+into that ABI.
+"""
+
+from .binding import (  # noqa: F401
+    PA_BF16,
+    PA_F16,
+    PA_FP8_E4M3,
+    PagedAttnError,
+    alloc_workspace,
+    decode_partition_size,
+    decode_workspace_bytes,
+    load_library,
+    pa_append_kv,
+    pa_decode,
+)

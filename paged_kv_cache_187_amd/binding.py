@@ -1,0 +1,149 @@
+"""ctypes binding of libpagedattn.so: argument marshalling only.
+
+Every function here takes torch tensors that already live on the GPU, checks
+that their shapes agree with each other, and passes raw device pointers and
+sizes to the C ABI with the current torch stream.  All computation runs in the
+library's HIP kernels; there is no fallback: if the library is missing or the
+GPU is absent, calls raise.
+"""
+
+import ctypes
+import os
+
+import torch
+
+from .build import LIB_PATH
+
+PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
+BLOCK_SIZE = 16
+
+_DTYPE = {torch.float16: PA_F16, torch.bfloat16: PA_BF16, torch.uint8: PA_FP8_E4M3,
+          torch.float8_e4m3fn: PA_FP8_E4M3}
+
+
+class PagedAttnError(RuntimeError):
+    """A pa_* call returned a non-zero pa_status."""
+
+    def __init__(self, status, message):
+        super().__init__(message)
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path=LIB_PATH):
+    """Load (once) and return the ctypes handle of the HIP library."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run `python -m paged_kv_cache_187_amd.build` "
+                           "or __graft_entry__.build() first")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.pa_append_kv.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i64, i32, i32, vp]
+    lib.pa_append_kv.restype = i32
+    lib.pa_decode_partition_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.pa_decode_partition_size.restype = i32
+    lib.pa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.pa_decode_workspace_bytes.restype = sz
+    lib.pa_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i64, i32, i32,
+                              ctypes.c_float, i32, i32, i32, vp, sz, vp]
+    lib.pa_decode.restype = i32
+    lib.pa_status_string.argtypes = [i32]
+    lib.pa_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status):
+    if status != 0:
+        msg = load_library().pa_status_string(status).decode()
+        raise PagedAttnError(status, msg)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _on_gpu(*tensors):
+    for t in tensors:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("paged attention tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("paged attention tensors must be contiguous")
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def pa_append_kv(key, value, key_cache, value_cache, slot_mapping, k_scale=None, v_scale=None, stream=None):
+    """Write key/value [T, Hkv, D] into the caches [nb, 16, Hkv, D] at slot_mapping [T] (int64).
+
+    FP8 caches (uint8 / float8_e4m3fn tensors) also take k_scale / v_scale [nb, 16] float32.
+    """
+    _on_gpu(key, value, key_cache, value_cache, slot_mapping, k_scale, v_scale)
+    T, hkv, d = key.shape
+    if value.shape != key.shape or key_cache.shape[1:] != (BLOCK_SIZE, hkv, d) or \
+            value_cache.shape != key_cache.shape or slot_mapping.shape != (T,) or \
+            slot_mapping.dtype != torch.int64:
+        raise ValueError("inconsistent shapes for pa_append_kv")
+    cdt = _DTYPE[key_cache.dtype]
+    if cdt == PA_FP8_E4M3:
+        for s in (k_scale, v_scale):
+            if s is None or s.dtype != torch.float32 or s.shape != key_cache.shape[:2]:
+                raise ValueError("FP8 cache needs float32 k_scale / v_scale shaped [num_blocks, 16]")
+    _check(load_library().pa_append_kv(
+        _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache), _ptr(k_scale), _ptr(v_scale),
+        _ptr(slot_mapping), T, hkv, d, key_cache.shape[0], _DTYPE[key.dtype], cdt, _stream(stream)))
+
+
+def decode_partition_size(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, partition_size=0):
+    return load_library().pa_decode_partition_size(num_seqs, num_heads, num_kv_heads, head_dim,
+                                                   max_context_len, partition_size)
+
+
+def decode_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, partition_size=0):
+    n = load_library().pa_decode_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim,
+                                                 max_context_len, partition_size)
+    if n == ctypes.c_size_t(-1).value:
+        raise PagedAttnError(2, "invalid arguments for pa_decode_workspace_bytes")
+    return n
+
+
+def alloc_workspace(query, num_kv_heads, max_context_len, partition_size=0):
+    """A workspace tensor sized for pa_decode with these arguments (None if none is needed)."""
+    B, hq, d = query.shape
+    n = decode_workspace_bytes(B, hq, num_kv_heads, d, max_context_len, partition_size)
+    return torch.empty(n, dtype=torch.uint8, device=query.device) if n else None
+
+
+def pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, scale, max_context_len,
+              partition_size=0, k_scale=None, v_scale=None, workspace=None, stream=None):
+    """Paged decode attention: out[B, Hq, D] <- attention of query[B, Hq, D] over the cached K/V.
+
+    block_tables [B, max_blocks] int32, context_lens [B] int32; max_context_len is a host-side
+    upper bound of context_lens.  A workspace is allocated here when none is passed.
+    """
+    _on_gpu(out, query, key_cache, value_cache, block_tables, context_lens, k_scale, v_scale, workspace)
+    B, hq, d = query.shape
+    nb, bs, hkv, dk = key_cache.shape
+    if out.shape != query.shape or out.dtype != query.dtype or bs != BLOCK_SIZE or dk != d or \
+            value_cache.shape != key_cache.shape or block_tables.dim() != 2 or \
+            block_tables.shape[0] != B or context_lens.shape != (B,) or \
+            block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("inconsistent shapes for pa_decode")
+    if workspace is None:
+        workspace = alloc_workspace(query, hkv, max_context_len, partition_size)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().pa_decode(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(k_scale), _ptr(v_scale),
+        _ptr(block_tables), _ptr(context_lens), B, hq, hkv, d, nb, block_tables.shape[1],
+        int(max_context_len), float(scale), int(partition_size), _DTYPE[query.dtype],
+        _DTYPE[key_cache.dtype], _ptr(workspace), ws_bytes, _stream(stream)))
+    return out

@@ -1,0 +1,47 @@
+// Host-side launchers behind the C ABI.  Arguments are already validated by
+// the entry points in pa_api.cpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+// Kind codes used between the C ABI and the launchers (same values as pa_dtype).
+enum Kind { kF16 = 0, kBF16 = 1, kFP8 = 2 };
+
+struct DecodeParams {
+    void* out;                 // [B, Hq, D] q dtype
+    const void* query;         // [B, Hq, D] q dtype
+    const void* key_cache;     // [num_blocks, 16, Hkv, D] cache dtype
+    const void* value_cache;
+    const float* k_scale;      // [num_blocks, 16] (FP8 cache)
+    const float* v_scale;
+    const int32_t* block_tables;  // [B, max_blocks]
+    const int32_t* context_lens;  // [B]
+    float* ws_acc;             // [B, Hq, NP, D]   (NP > 1 only)
+    float* ws_ml;              // [B, Hq, NP, 2]
+    int64_t num_blocks;
+    int32_t B, Hq, Hkv, max_blocks, ctx_limit;  // ctx_limit = min(max_context_len, 16 * max_blocks)
+    int32_t NP;                // partitions per sequence in the grid
+    int32_t part_blocks;       // partition length in 16-token blocks
+    int32_t groups;            // head groups per sequence = Hq / heads_per_wg
+    float scale_log2;          // softmax scale * log2(e)
+};
+
+hipError_t launch_append_copy(const void* key, const void* value, void* key_cache, void* value_cache,
+                              const int64_t* slots, int64_t num_tokens, int32_t row_bytes,
+                              int64_t num_slots, hipStream_t stream);
+
+hipError_t launch_append_fp8(const void* key, const void* value, void* key_cache, void* value_cache,
+                             float* k_scale, float* v_scale, const int64_t* slots, int64_t num_tokens,
+                             int32_t row_elems, int64_t num_slots, int src_kind, hipStream_t stream);
+
+// Heads of one KV head handled together by one workgroup (largest of 8,4,2,1
+// dividing the group size).
+int heads_per_workgroup(int group);
+
+hipError_t launch_decode(const DecodeParams& p, int head_dim, int q_kind, int cache_kind, int heads_per_wg,
+                         hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,106 @@
+"""GPU parity of the slot-mapped append: bit-exact against the oracle on the whole pool."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_187_amd as pa
+import synth
+from synth import bits_np
+
+from gpu_cases import oracle_caches, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def test_append_tiny_whole_pool_bit_exact():
+    _say("append tiny f16")
+    wh = synth.make_workload("tiny")
+    w = to_device(wh)
+    pa.pa_append_kv(w.key_new, w.value_new, w.key_cache, w.value_cache, w.slot_mapping)
+    torch.cuda.synchronize()
+    kc, vc, _, _ = oracle_caches(wh)
+    assert np.array_equal(bits_np(w.key_cache), kc)
+    assert np.array_equal(bits_np(w.value_cache), vc)
+
+
+@pytest.mark.parametrize("dtype,hkv,d", [("bf16", 8, 128), ("f16", 3, 64), ("bf16", 1, 64), ("f16", 32, 128)])
+def test_append_ragged_slots_bit_exact(dtype, hkv, d):
+    _say(f"append {dtype} hkv={hkv} d={d}")
+    nb, T = 9, 41
+    tdt = torch.float16 if dtype == "f16" else torch.bfloat16
+    g = torch.Generator().manual_seed(hkv * d)
+    kc = torch.randn(nb, 16, hkv, d, generator=g).to(tdt)
+    vc = torch.randn(nb, 16, hkv, d, generator=g).to(tdt)
+    k = torch.randn(T, hkv, d, generator=g).to(tdt)
+    v = torch.randn(T, hkv, d, generator=g).to(tdt)
+    rng = np.random.default_rng(d)
+    slots = rng.permutation(nb * 16)[:T].astype(np.int64)
+    slots[::7] = -1                                   # skipped
+    slots[3] = nb * 16                                # past the pool: skipped
+    slots[5] = nb * 16 + 1000
+    slots[6] = -(1 << 40)
+    ek, ev = oracle.append_kv(bits_np(kc), bits_np(vc), bits_np(k), bits_np(v), slots)
+    kcd, vcd = kc.cuda(), vc.cuda()
+    pa.pa_append_kv(k.cuda(), v.cuda(), kcd, vcd, torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_np(kcd), ek)
+    assert np.array_equal(bits_np(vcd), ev)
+
+
+def _small_fp8_cfg(**kw):
+    base = dict(name="fp8small", num_seqs=8, num_heads=8, num_kv_heads=2, head_dim=128, q_dtype="bf16",
+                cache_dtype="fp8_e4m3", lengths="beams", len_args=(83,), seed=77, beams=4, prefix_len=48)
+    base.update(kw)
+    return synth.DecodeConfig(**base)
+
+
+@pytest.mark.parametrize("q_dtype,d", [("bf16", 128), ("f16", 64)])
+def test_quantising_append_bit_exact(q_dtype, d):
+    _say(f"fp8 append src={q_dtype} d={d}")
+    wh = synth.make_workload(_small_fp8_cfg(q_dtype=q_dtype, head_dim=d))
+    w = to_device(wh)
+    pa.pa_append_kv(w.fill_key, w.fill_value, w.key_cache, w.value_cache, w.fill_slots, w.k_scale, w.v_scale)
+    pa.pa_append_kv(w.key_new, w.value_new, w.key_cache, w.value_cache, w.slot_mapping, w.k_scale, w.v_scale)
+    torch.cuda.synchronize()
+    kc, vc, ks, vs = oracle_caches(wh)
+    assert np.array_equal(bits_np(w.key_cache), kc)
+    assert np.array_equal(bits_np(w.value_cache), vc)
+    # scales: bitwise, NaN (untouched) included
+    assert np.array_equal(w.k_scale.cpu().numpy().view(np.uint32), ks.view(np.uint32))
+    assert np.array_equal(w.v_scale.cpu().numpy().view(np.uint32), vs.view(np.uint32))
+
+
+@pytest.mark.parametrize("src", ["bf16", "f16"])
+def test_quantiser_every_representable_source_value(src):
+    """Rows whose amax is 448 (scale exactly 1) carrying every finite source value with |x| <= 448."""
+    _say(f"fp8 encoder exhaustive over {src}")
+    tdt = torch.bfloat16 if src == "bf16" else torch.float16
+    pats = torch.from_numpy(np.arange(1 << 16, dtype=np.uint16).view(np.int16)).view(tdt)
+    vals = pats[torch.isfinite(pats.float()) & (pats.float().abs() <= 448)]
+    hkv, d = 16, 128
+    per_row = hkv * d - 1
+    rows = -(-vals.numel() // per_row)
+    data = torch.zeros(rows * per_row, dtype=tdt)
+    data[:vals.numel()] = vals
+    data = data.view(rows, per_row)
+    data = torch.cat([torch.full((rows, 1), 448.0, dtype=tdt), data], dim=1).view(rows, hkv, d)
+    nb = -(-rows // 16)
+    kc = torch.full((nb, 16, hkv, d), 0x7F, dtype=torch.uint8)
+    ks = torch.full((nb, 16), float("nan"))
+    slots = np.arange(rows, dtype=np.int64)
+    ek, ev, eks, evs = oracle.append_kv_e4m3(bits_np(kc), bits_np(kc), ks.numpy(), ks.numpy(), bits_np(data),
+                                             bits_np(data), src, slots)
+    assert np.all(eks[:rows // 16] == 1.0)
+    kcd, vcd, ksd, vsd = kc.cuda(), kc.clone().cuda(), ks.cuda(), ks.clone().cuda()
+    dd = data.cuda()
+    pa.pa_append_kv(dd, dd, kcd, vcd, torch.from_numpy(slots).cuda(), ksd, vsd)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_np(kcd), ek)
+    assert np.array_equal(bits_np(vcd), ev)
+    assert np.array_equal(ksd.cpu().numpy().view(np.uint32), eks.view(np.uint32))
