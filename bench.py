@@ -1,0 +1,265 @@
+"""Benchmark: one decode step of paged attention on one MI355X.
+
+A step is the whole hot path over one batch: the slot-mapped append of each
+sequence's new token, then paged decode attention over every sequence's cache
+(split over partitions and merged when a sequence is longer than one
+partition).  The default workload is the LLaMA-7B-shaped single layer: B=32
+sequences, 32 query / 32 KV heads, head_dim 128, f16 cache, 16-token blocks,
+context lengths uniform in [1, 2048], pool = blocks in use + 10 %, physical
+blocks in seeded random order.  Inputs are synthetic (seeded N(0,1)).
+
+Timing: W untimed steps, then K timed steps between two device
+synchronisations; each step uses the next of R pool replicas (R * pool bytes
+well above the 256 MB Infinity Cache), so the KV bytes come from HBM.  HIP
+events on the launch stream bracket every decode call for the roofline line.
+
+Prints one JSON line.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention: tokens/s and effective HBM GB/s (% of peak), 1×MI355X"
+HBM_PEAK_GBS = 8000.0
+
+WORKLOAD_TEXT = {
+    "llama7b": "LLaMA-7B-shaped single-layer paged decode: B=32, Hq=Hkv=32, D=128, f16 KV/Q, fp32 accumulate, "
+               "16-token blocks, context lens U[1,2048], pool +10%, permuted blocks",
+    "gqa70b": "GQA 70B-shaped single layer: B=64, Hq=64, Hkv=8, D=128, bf16, 16-token blocks, context lens "
+              "lognormal (median 1024, sigma 1, clip [16,4096]), pool +10%, permuted blocks",
+    "longctx": "long-context split-K decode: B=8, Hq=Hkv=32, D=128, f16, context lens U[32768,131072], "
+               "512-token partitions",
+    "fp8beams": "fp8-e4m3 KV with per-token scales, 16 prompts x 4 beams sharing 1024-token prefixes + 256 "
+                "private tokens, Hq=32, Hkv=8, D=128, Q bf16",
+    "tiny": "tiny paged decode: B=4, lens {1,17,33,50}, Hq=Hkv=4, D=64, f16",
+}
+
+
+def algorithmic_bytes(w):
+    """Bytes the method must read per decode: KV rows + scales, Q, page-table entries, lengths."""
+    import numpy as np
+    cfg = w.cfg
+    eb = 1 if cfg.cache_dtype == "fp8_e4m3" else 2
+    lens = w.lens_np.astype(np.int64)
+    if cfg.beams > 1:
+        # unique bytes: shared prefix blocks counted once
+        prompts = cfg.num_seqs // cfg.beams
+        tokens = prompts * cfg.prefix_len + int(np.sum(lens - cfg.prefix_len))
+    else:
+        tokens = int(lens.sum())
+    kv = tokens * cfg.num_kv_heads * cfg.head_dim * 2 * eb
+    if eb == 1:
+        kv += tokens * 8
+    q = cfg.num_seqs * cfg.num_heads * cfg.head_dim * 2
+    table = int(np.sum((lens + 15) // 16)) * 4 + cfg.num_seqs * 4
+    return kv + q + table
+
+
+def time_workload(name, steps, warmup, replicas, snapshot=False, partition_size=None):
+    import torch
+    import paged_kv_cache_187_amd as pa
+    import synth
+    from synth import bits_np
+
+    overrides = {} if partition_size is None else {"partition_size": partition_size}
+    w = synth.make_workload(name, device="cuda", **overrides)
+    cfg = w.cfg
+    host = None
+    if snapshot:   # pre-step host copies for the CPU baseline
+        host = {"query": bits_np(w.query), "key_cache": bits_np(w.key_cache),
+                "value_cache": bits_np(w.value_cache), "key_new": bits_np(w.key_new),
+                "value_new": bits_np(w.value_new), "slot_mapping": w.slot_mapping.cpu().numpy()}
+    kcs = [w.key_cache] + [w.key_cache.clone() for _ in range(replicas - 1)]
+    vcs = [w.value_cache] + [w.value_cache.clone() for _ in range(replicas - 1)]
+    kss = [w.k_scale] + [None if w.k_scale is None else w.k_scale.clone() for _ in range(replicas - 1)]
+    vss = [w.v_scale] + [None if w.v_scale is None else w.v_scale.clone() for _ in range(replicas - 1)]
+    if w.fill_slots is not None:
+        for r in range(replicas):
+            pa.pa_append_kv(w.fill_key, w.fill_value, kcs[r], vcs[r], w.fill_slots, kss[r], vss[r])
+    part = cfg.partition_size
+    ws = pa.alloc_workspace(w.query, cfg.num_kv_heads, w.max_context_len, part)
+    out = torch.empty_like(w.query)
+    stream = torch.cuda.current_stream()
+    max_len = w.max_context_len
+
+    def step(i, ev=None):
+        r = i % replicas
+        pa.pa_append_kv(w.key_new, w.value_new, kcs[r], vcs[r], w.slot_mapping, kss[r], vss[r])
+        if ev is not None:
+            ev[0].record(stream)
+        pa.pa_decode(out, w.query, kcs[r], vcs[r], w.block_tables, w.context_lens, cfg.scale, max_len,
+                     partition_size=part, k_scale=kss[r], v_scale=vss[r], workspace=ws)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(warmup + i, events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    dec_ms = sorted(e[0].elapsed_time(e[1]) for e in events)
+    n = len(dec_ms)
+    return {
+        "w": w,
+        "host": host,
+        "ms_per_step": (t1 - t0) * 1e3 / steps,
+        "decode_ms_mean": sum(dec_ms) / n,
+        "decode_ms_p10": dec_ms[n // 10],
+        "decode_ms_p50": dec_ms[n // 2],
+        "decode_ms_p90": dec_ms[min(n - 1, (9 * n) // 10)],
+        "partition_size": pa.decode_partition_size(cfg.num_seqs, cfg.num_heads, cfg.num_kv_heads, cfg.head_dim,
+                                                   max_len, part),
+        "bytes": algorithmic_bytes(w),
+    }
+
+
+def cpu_baseline(w, host, min_seconds):
+    """The float64 oracle on the host, on the same workload (pre-step state), single-threaded."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    cfg = w.cfg
+    q = host["query"]
+    kc0, vc0 = host["key_cache"], host["value_cache"]
+    kn, vn, slots = host["key_new"], host["value_new"], host["slot_mapping"]
+    reps = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while True:
+            kc, vc = oracle.append_kv(kc0, vc0, kn, vn, slots)
+            out = oracle.paged_decode(q, kc, vc, w.tables_np, w.lens_np, cfg.scale, cfg.q_dtype, cfg.cache_dtype)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= min_seconds:
+                break
+    assert np.all(np.isfinite(out))
+    return {
+        "value": round(cfg.num_seqs * reps / el, 3),
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{reps} full step(s) of the {cfg.name} workload (append of {cfg.num_seqs} tokens + float64 "
+                  f"decode of all {cfg.num_seqs}x{cfg.num_heads} (sequence, head) pairs) in {el:.1f} s, "
+                  f"numpy/BLAS limited to 1 thread",
+    }
+
+
+def summarize(name, r):
+    achieved = r["bytes"] / (r["decode_ms_mean"] * 1e-3) / 1e9
+    cfg = r["w"].cfg
+    return {
+        "workload": name,
+        "tokens_per_s": round(cfg.num_seqs / (r["ms_per_step"] * 1e-3), 1),
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "decode_us_mean": round(r["decode_ms_mean"] * 1e3, 2),
+        "decode_us_p10_p50_p90": [round(r[k] * 1e3, 2) for k in ("decode_ms_p10", "decode_ms_p50", "decode_ms_p90")],
+        "algorithmic_bytes": r["bytes"],
+        "effective_GBs": round(achieved, 1),
+        "frac_of_peak": round(achieved / HBM_PEAK_GBS, 4),
+        "partition_size": r["partition_size"],
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama7b")
+    ap.add_argument("--replicas", type=int, default=3, help="pool replicas rotated across steps")
+    ap.add_argument("--also", default="gqa70b", help="comma-separated extra workloads reported alongside")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (5 times), to scale rocprofv3 FETCH_SIZE/WRITE_SIZE")
+    ap.add_argument("--partition-size", type=int, default=None,
+                    help="override the workload's partition length (tokens; 0 = library's choice)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (this build has no "
+              "multi-GPU path; the paged decode would shard by sequence or KV head with no exchange)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.calibrate_copy:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read_per_copy": 1 << 30,
+                          "bytes_written_per_copy": 1 << 30, "copies": 5}), flush=True)
+        return
+
+    import paged_kv_cache_187_amd as pa
+    pa.load_library()
+
+    main_r = time_workload(args.workload, args.steps, args.warmup, args.replicas,
+                           snapshot=not args.no_cpu_baseline, partition_size=args.partition_size)
+    s = summarize(args.workload, main_r)
+    cfg = main_r["w"].cfg
+    also = {}
+    for name in [n for n in args.also.split(",") if n and n != args.workload]:
+        r = time_workload(name, args.steps, args.warmup, args.replicas, partition_size=args.partition_size)
+        also[name] = summarize(name, r)
+        del r
+        torch.cuda.empty_cache()
+
+    result = {
+        "metric": METRIC,
+        "value": s["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": s["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.cache_dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": WORKLOAD_TEXT.get(args.workload, args.workload),
+            "num_seqs": cfg.num_seqs, "num_heads": cfg.num_heads, "num_kv_heads": cfg.num_kv_heads,
+            "head_dim": cfg.head_dim, "block_size": 16, "kv_dtype": cfg.cache_dtype, "q_dtype": cfg.q_dtype,
+            "accumulate": "f32", "partition_size": s["partition_size"], "pool_replicas": args.replicas,
+            "tokens_in_cache": int(main_r["w"].lens_np.sum()),
+        },
+        "roofline": {
+            "kernel": "pa_decode (decode_partition_kernel + decode_reduce_kernel)",
+            "bound": "hbm",
+            "achieved": s["effective_GBs"],
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": s["frac_of_peak"],
+            "traffic": None,
+            "bytes_per_launch": s["algorithmic_bytes"],
+            "launch_us_mean": s["decode_us_mean"],
+            "launch_us_p10_p50_p90": s["decode_us_p10_p50_p90"],
+        },
+        "also": also,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(main_r["w"], main_r["host"], args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -110,11 +110,13 @@ pa_status pa_append_kv(const void *key, const void *value,
                        void *stream);
 
 /*
- * pa_decode_partition_size - the partition (split-K chunk) length, in tokens,
- * that pa_decode uses for these arguments: `partition_size` itself when it is
- * non-zero, otherwise the library's choice for this batch shape.  Returns 0
- * when the arguments are invalid (partition_size not a positive multiple of
- * 16 and not 0, or a non-positive size).
+ * pa_decode_partition_size - how pa_decode splits the work for these
+ * arguments.  partition_size > 0 (a multiple of 16, at most 2^20): fixed
+ * partitions of that many tokens, one wave per (sequence, head group,
+ * partition); the function returns partition_size.  partition_size == 0:
+ * the balanced split, which cuts the (sequence, head group, 16-token block)
+ * space into equal ranges, one per wave, whatever the length mix; the
+ * function returns 0.  Returns -1 when the arguments are invalid.
  */
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_context_len,
@@ -122,11 +124,11 @@ int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_heads, int32_t nu
 
 /*
  * pa_decode_workspace_bytes - device workspace pa_decode needs for these
- * arguments (0 when a single partition covers max_context_len, so no
- * cross-partition reduction is needed; (size_t)-1 for invalid arguments).
- * Layout: float32 partial sums [num_seqs, num_heads, P, head_dim] followed by
- * float32 (max, sum) pairs [num_seqs, num_heads, P, 2], where
- * P = ceil(max_context_len / partition length).
+ * arguments ((size_t)-1 for invalid arguments; 0 when nothing is split,
+ * i.e. fixed partitions with max_context_len <= partition_size).  The
+ * workspace holds float32 partial results: per (slot, head of the group) a
+ * V sum of head_dim floats, followed by all (max, sum of exponentials)
+ * pairs.  Its contents need no initialisation and are scratch after the call.
  */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_context_len,
@@ -145,11 +147,12 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t nu
  * even).  L == 0 gives a zero row.  Only slots t < L are read: whatever the
  * other slots and the table entries past ceil(L/16) hold never reaches out.
  *
- * Sequences longer than one partition are split into partitions of
- * pa_decode_partition_size(...) tokens whose partial results (running max,
- * sum of exponentials, weighted V sum) go to `workspace` and are merged in
- * ascending partition order, so for fixed inputs and partition size the
- * output is bitwise deterministic.
+ * Work is split over waves as pa_decode_partition_size describes; a
+ * sequence covered by more than one wave gets partial results (running
+ * max, sum of exponentials, weighted V sum) in `workspace` that a second
+ * kernel merges in ascending token order, so for fixed inputs and fixed
+ * (num_seqs, num_heads, num_kv_heads, head_dim, max_context_len,
+ * partition_size) the output is bitwise deterministic.
  *
  * Supported (q_dtype, cache_dtype): (F16, F16), (BF16, BF16), (F16, FP8_E4M3),
  * (BF16, FP8_E4M3).  head_dim 64 or 128.  num_heads a multiple of

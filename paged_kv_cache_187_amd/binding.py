@@ -104,6 +104,7 @@ def pa_append_kv(key, value, key_cache, value_cache, slot_mapping, k_scale=None,
 
 
 def decode_partition_size(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, partition_size=0):
+    """Fixed partition length in tokens, 0 for the balanced split, -1 for invalid arguments."""
     return load_library().pa_decode_partition_size(num_seqs, num_heads, num_kv_heads, head_dim,
                                                    max_context_len, partition_size)
 

@@ -13,21 +13,57 @@
 
 namespace {
 
-constexpr int32_t kDefaultPartition = 512;       // tokens; 32 blocks
 constexpr int32_t kMaxPartition = 1 << 20;
-constexpr int64_t kMaxGrid = (int64_t)1 << 31;   // workgroups per launch
+constexpr int64_t kMaxWork = ((int64_t)1 << 30);  // waves, or (head group, block) pairs, per launch
+constexpr int64_t kBalancedWaves = 2048;            // waves of the balanced split (8 per CU)
+
+// Launch shape shared by pa_decode and pa_decode_workspace_bytes.
+struct Plan {
+    bool ok;
+    bool balanced;
+    int64_t part;        // fixed split: partition tokens
+    int64_t np;          // fixed split: partitions per sequence
+    int64_t hpw;         // heads per wave
+    int64_t groups;      // head groups per sequence
+    int64_t waves;       // waves in the grid
+    int64_t slots;       // workspace slots (each HPW heads x (D + 2) floats)
+};
+
+Plan make_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+               int32_t max_context_len, int32_t partition_size) {
+    Plan pl{};
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 || head_dim <= 0 ||
+        max_context_len < 0 || partition_size < 0 || partition_size % PA_BLOCK_SIZE != 0 ||
+        partition_size > kMaxPartition)
+        return pl;
+    pl.hpw = pa::heads_per_workgroup(num_heads / num_kv_heads);
+    pl.groups = num_heads / pl.hpw;
+    const int64_t seq_groups = (int64_t)num_seqs * pl.groups;
+    const int64_t max_blocks = (max_context_len + PA_BLOCK_SIZE - 1) / PA_BLOCK_SIZE;
+    if (seq_groups * (max_blocks > 0 ? max_blocks : 1) >= kMaxWork) return pl;
+    pl.balanced = partition_size == 0;
+    if (pl.balanced) {
+        const int64_t work = seq_groups * max_blocks;   // upper bound of (head group, block) pairs
+        pl.waves = work < kBalancedWaves ? (work > 0 ? work : 1) : kBalancedWaves;
+        pl.slots = pl.waves + seq_groups;
+    } else {
+        pl.part = partition_size;
+        pl.np = (max_context_len + partition_size - 1) / partition_size;
+        if (pl.np < 1) pl.np = 1;
+        pl.waves = pl.np * seq_groups;
+        pl.slots = pl.np > 1 ? pl.np * seq_groups : 0;
+    }
+    pl.ok = pl.waves < kMaxWork;
+    return pl;
+}
+
+size_t workspace_size(const Plan& pl, int32_t head_dim) {
+    return (size_t)pl.slots * (size_t)pl.hpw * (size_t)(head_dim + 2) * sizeof(float);
+}
 
 bool aligned(const void* ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) == 0; }
 
 bool is16(int32_t d) { return d == PA_F16 || d == PA_BF16; }
-
-int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
-
-// Partition count of the grid; at least one so that L == 0 rows get written.
-int64_t num_partitions(int32_t max_context_len, int32_t part) {
-    const int64_t n = ceil_div(max_context_len, part);
-    return n < 1 ? 1 : n;
-}
 
 pa_status from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
 
@@ -79,22 +115,16 @@ pa_status pa_append_kv(const void* key, const void* value, void* key_cache, void
 
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                                  int32_t max_context_len, int32_t partition_size) {
-    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_context_len < 0) return 0;
-    if (partition_size != 0) {
-        if (partition_size < 0 || partition_size % PA_BLOCK_SIZE != 0 || partition_size > kMaxPartition) return 0;
-        return partition_size;
-    }
-    return kDefaultPartition;
+    const Plan pl = make_plan(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, partition_size);
+    if (!pl.ok) return -1;
+    return pl.balanced ? 0 : (int32_t)pl.part;
 }
 
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                                  int32_t max_context_len, int32_t partition_size) {
-    const int32_t part = pa_decode_partition_size(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len,
-                                                  partition_size);
-    if (part <= 0) return (size_t)-1;
-    const int64_t np = num_partitions(max_context_len, part);
-    if (np <= 1) return 0;
-    return (size_t)num_seqs * (size_t)num_heads * (size_t)np * (size_t)(head_dim + 2) * sizeof(float);
+    const Plan pl = make_plan(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, partition_size);
+    if (!pl.ok) return (size_t)-1;
+    return workspace_size(pl, head_dim);
 }
 
 pa_status pa_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
@@ -111,11 +141,9 @@ pa_status pa_decode(void* out, const void* query, const void* key_cache, const v
     const bool fp8 = cache_dtype == PA_FP8_E4M3;
     if (!fp8 && cache_dtype != q_dtype) return PA_ERR_DTYPE;
     if (!std::isfinite(scale)) return PA_ERR_SHAPE;
-    const int32_t part = pa_decode_partition_size(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len,
-                                                  partition_size);
-    if (part <= 0) return PA_ERR_SHAPE;
-    const size_t need = pa_decode_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len,
-                                                  partition_size);
+    const Plan pl = make_plan(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, partition_size);
+    if (!pl.ok) return PA_ERR_SHAPE;
+    const size_t need = workspace_size(pl, head_dim);
     if (num_seqs == 0) return PA_OK;
     if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens) return PA_ERR_NULL;
     if (fp8 && (!k_scale || !v_scale)) return PA_ERR_NULL;
@@ -124,12 +152,6 @@ pa_status pa_decode(void* out, const void* query, const void* key_cache, const v
         !aligned(block_tables, 4) || !aligned(context_lens, 4) || (need > 0 && !aligned(workspace, 16)) ||
         (fp8 && (!aligned(k_scale, 4) || !aligned(v_scale, 4))))
         return PA_ERR_ALIGN;
-
-    const int group = num_heads / num_kv_heads;
-    const int hpw = pa::heads_per_workgroup(group);
-    const int64_t np = num_partitions(max_context_len, part);
-    const int64_t groups = num_heads / hpw;
-    if (np * groups * num_seqs >= kMaxGrid) return PA_ERR_SHAPE;
 
     pa::DecodeParams p{};
     p.out = out;
@@ -141,7 +163,7 @@ pa_status pa_decode(void* out, const void* query, const void* key_cache, const v
     p.block_tables = block_tables;
     p.context_lens = context_lens;
     p.ws_acc = need > 0 ? (float*)workspace : nullptr;
-    p.ws_ml = need > 0 ? (float*)workspace + (size_t)num_seqs * num_heads * np * head_dim : nullptr;
+    p.ws_ml = need > 0 ? (float*)workspace + (size_t)pl.slots * pl.hpw * head_dim : nullptr;
     p.num_blocks = num_blocks;
     p.B = num_seqs;
     p.Hq = num_heads;
@@ -149,11 +171,13 @@ pa_status pa_decode(void* out, const void* query, const void* key_cache, const v
     p.max_blocks = max_blocks_per_seq;
     const int64_t table_tokens = (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE;
     p.ctx_limit = (int32_t)(table_tokens < max_context_len ? table_tokens : max_context_len);
-    p.NP = (int32_t)np;
-    p.part_blocks = part / PA_BLOCK_SIZE;
-    p.groups = (int32_t)groups;
+    p.balanced = pl.balanced ? 1 : 0;
+    p.NP = (int32_t)pl.np;
+    p.part_blocks = (int32_t)(pl.part / PA_BLOCK_SIZE);
+    p.groups = (int32_t)pl.groups;
+    p.num_waves = (int32_t)pl.waves;
     p.scale_log2 = scale * 1.4426950408889634f;
-    return from_hip(pa::launch_decode(p, head_dim, q_dtype, cache_dtype, hpw, (hipStream_t)stream));
+    return from_hip(pa::launch_decode(p, head_dim, q_dtype, cache_dtype, (int)pl.hpw, (hipStream_t)stream));
 }
 
 }  // extern "C"

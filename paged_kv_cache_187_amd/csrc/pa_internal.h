@@ -19,13 +19,15 @@ struct DecodeParams {
     const float* v_scale;
     const int32_t* block_tables;  // [B, max_blocks]
     const int32_t* context_lens;  // [B]
-    float* ws_acc;             // [B, Hq, NP, D]   (NP > 1 only)
-    float* ws_ml;              // [B, Hq, NP, 2]
+    float* ws_acc;             // [slots, HPW, D] partial V sums
+    float* ws_ml;              // [slots, HPW, 2] partial (max, sum of exponentials)
     int64_t num_blocks;
     int32_t B, Hq, Hkv, max_blocks, ctx_limit;  // ctx_limit = min(max_context_len, 16 * max_blocks)
-    int32_t NP;                // partitions per sequence in the grid
-    int32_t part_blocks;       // partition length in 16-token blocks
-    int32_t groups;            // head groups per sequence = Hq / heads_per_wg
+    int32_t balanced;          // 1: equal (sequence, head group, block) ranges per wave
+    int32_t NP;                // fixed split: partitions per sequence in the grid
+    int32_t part_blocks;       // fixed split: partition length in 16-token blocks
+    int32_t groups;            // head groups per sequence = Hq / heads per wave
+    int32_t num_waves;         // waves in the grid
     float scale_log2;          // softmax scale * log2(e)
 };
 
@@ -37,8 +39,8 @@ hipError_t launch_append_fp8(const void* key, const void* value, void* key_cache
                              float* k_scale, float* v_scale, const int64_t* slots, int64_t num_tokens,
                              int32_t row_elems, int64_t num_slots, int src_kind, hipStream_t stream);
 
-// Heads of one KV head handled together by one workgroup (largest of 8,4,2,1
-// dividing the group size).
+// Query heads of one KV head handled together by one wave (largest of 8, 4,
+// 2, 1 dividing the group size).
 int heads_per_workgroup(int group);
 
 hipError_t launch_decode(const DecodeParams& p, int head_dim, int q_kind, int cache_kind, int heads_per_wg,

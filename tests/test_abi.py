@@ -55,12 +55,16 @@ def test_status_strings(lib):
 
 def test_partition_and_workspace_sizes(lib):
     assert lib.pa_decode_partition_size(8, 32, 32, 128, 131072, 512) == 512
-    assert lib.pa_decode_partition_size(8, 32, 32, 128, 131072, 0) > 0
-    assert lib.pa_decode_partition_size(8, 32, 32, 128, 131072, 24) == 0      # not a multiple of 16
-    assert lib.pa_decode_partition_size(8, 32, 32, 128, 131072, -16) == 0
+    assert lib.pa_decode_partition_size(8, 32, 32, 128, 131072, 0) == 0       # balanced split
+    assert lib.pa_decode_partition_size(8, 32, 32, 128, 131072, 24) == -1     # not a multiple of 16
+    assert lib.pa_decode_partition_size(8, 32, 32, 128, 131072, -16) == -1
+    assert lib.pa_decode_partition_size(8, 32, 24, 128, 131072, 0) == -1      # heads not a multiple
     # 131072 / 512 = 256 partitions of (128 + 2) floats per (seq, head)
     assert pa.decode_workspace_bytes(8, 32, 32, 128, 131072, 512) == 8 * 32 * 256 * 130 * 4
     assert pa.decode_workspace_bytes(4, 4, 4, 64, 50, 512) == 0               # one partition: none
+    # balanced: one slot per wave plus one per (sequence, head group); GQA 8 heads per wave
+    n = pa.decode_workspace_bytes(64, 64, 8, 128, 4096, 0)
+    assert n > 0 and n % (8 * 130 * 4) == 0
     with pytest.raises(pa.PagedAttnError):
         pa.decode_workspace_bytes(4, 4, 4, 64, 50, 17)
 
@@ -92,7 +96,9 @@ def test_decode_host_checks(lib):
     assert _decode(lib, qd=3, cd=3) == DTYPE
     assert _decode(lib, maxL=4096, part=512) == WS          # 8 partitions need a workspace
     assert _decode(lib, maxL=4096, part=512, ws=FAKE, wsb=100) == WS
-    assert _decode(lib, out=FAKE + 2) == ALIGN
+    assert _decode(lib, part=0) == WS                       # the balanced split always merges
+    assert _decode(lib, out=FAKE + 2, ws=FAKE, wsb=1 << 30) == ALIGN
+    assert _decode(lib, ws=FAKE + 4, wsb=1 << 30) == ALIGN
     assert _decode(lib, B=0) == OK                          # nothing to do, nothing launched
 
 
