@@ -10,8 +10,10 @@ blocks in seeded random order.  Inputs are synthetic (seeded N(0,1)).
 
 Timing: W untimed steps, then K timed steps between two device
 synchronisations; each step uses the next of R pool replicas (R * pool bytes
-well above the 256 MB Infinity Cache), so the KV bytes come from HBM.  HIP
-events on the launch stream bracket every decode call for the roofline line.
+well above the 256 MB Infinity Cache), so the KV bytes come from HBM.  Kernels
+are launched from Python on torch's current stream (--graphs replays captured
+HIP graphs of the same launches instead).  HIP events on the launch stream
+bracket every decode call for the roofline line.
 
 Prints one JSON line.
 """
@@ -61,7 +63,7 @@ def algorithmic_bytes(w):
     return kv + q + table
 
 
-def time_workload(name, steps, warmup, replicas, snapshot=False, partition_size=None):
+def time_workload(name, steps, warmup, replicas, snapshot=False, partition_size=None, use_graphs=False):
     import torch
     import paged_kv_cache_187_amd as pa
     import synth
@@ -85,27 +87,48 @@ def time_workload(name, steps, warmup, replicas, snapshot=False, partition_size=
     part = cfg.partition_size
     ws = pa.alloc_workspace(w.query, cfg.num_kv_heads, w.max_context_len, part)
     out = torch.empty_like(w.query)
-    stream = torch.cuda.current_stream()
     max_len = w.max_context_len
 
-    def step(i, ev=None):
-        r = i % replicas
+    def append(r):
         pa.pa_append_kv(w.key_new, w.value_new, kcs[r], vcs[r], w.slot_mapping, kss[r], vss[r])
-        if ev is not None:
-            ev[0].record(stream)
+
+    def decode(r):
         pa.pa_decode(out, w.query, kcs[r], vcs[r], w.block_tables, w.context_lens, cfg.scale, max_len,
                      partition_size=part, k_scale=kss[r], v_scale=vss[r], workspace=ws)
-        if ev is not None:
-            ev[1].record(stream)
 
     for i in range(warmup):
-        step(i)
+        append(i % replicas)
+        decode(i % replicas)
     torch.cuda.synchronize()
+    if use_graphs:
+        # One HIP graph per replica for the append and one for the decode: replaying them keeps
+        # the host from pacing the GPU, and the decode replay stays separately timeable.
+        graphs = []
+        for r in range(replicas):
+            ga, gd = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+            with torch.cuda.graph(ga):
+                append(r)
+            with torch.cuda.graph(gd):
+                decode(r)
+            graphs.append((ga, gd))
+        run_append = lambda r: graphs[r][0].replay()
+        run_decode = lambda r: graphs[r][1].replay()
+        for i in range(warmup):
+            run_append(i % replicas)
+            run_decode(i % replicas)
+    else:
+        run_append, run_decode = append, decode
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
     events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step(warmup + i, events[i])
+        r = (warmup + i) % replicas
+        run_append(r)
+        events[i][0].record(stream)
+        run_decode(r)
+        events[i][1].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     dec_ms = sorted(e[0].elapsed_time(e[1]) for e in events)
@@ -183,6 +206,8 @@ def main():
     ap.add_argument("--also", default="gqa70b", help="comma-separated extra workloads reported alongside")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graphs", action="store_true", help="replay captured HIP graphs of each replica's append "
+                    "and decode instead of launching from Python (slower on ROCm 7 for this two-launch step)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (5 times), to scale rocprofv3 FETCH_SIZE/WRITE_SIZE")
     ap.add_argument("--partition-size", type=int, default=None,
@@ -212,12 +237,14 @@ def main():
     pa.load_library()
 
     main_r = time_workload(args.workload, args.steps, args.warmup, args.replicas,
-                           snapshot=not args.no_cpu_baseline, partition_size=args.partition_size)
+                           snapshot=not args.no_cpu_baseline, partition_size=args.partition_size,
+                           use_graphs=args.graphs)
     s = summarize(args.workload, main_r)
     cfg = main_r["w"].cfg
     also = {}
     for name in [n for n in args.also.split(",") if n and n != args.workload]:
-        r = time_workload(name, args.steps, args.warmup, args.replicas, partition_size=args.partition_size)
+        r = time_workload(name, args.steps, args.warmup, args.replicas, partition_size=args.partition_size,
+                          use_graphs=args.graphs)
         also[name] = summarize(name, r)
         del r
         torch.cuda.empty_cache()
@@ -240,6 +267,7 @@ def main():
             "num_seqs": cfg.num_seqs, "num_heads": cfg.num_heads, "num_kv_heads": cfg.num_kv_heads,
             "head_dim": cfg.head_dim, "block_size": 16, "kv_dtype": cfg.cache_dtype, "q_dtype": cfg.q_dtype,
             "accumulate": "f32", "partition_size": s["partition_size"], "pool_replicas": args.replicas,
+            "hip_graphs": args.graphs,
             "tokens_in_cache": int(main_r["w"].lens_np.sum()),
         },
         "roofline": {

@@ -24,6 +24,7 @@ struct Plan {
     int64_t part;        // fixed split: partition tokens
     int64_t np;          // fixed split: partitions per sequence
     int64_t hpw;         // heads per wave
+    bool mfma;           // matrix-core path
     int64_t groups;      // head groups per sequence
     int64_t waves;       // waves in the grid
     int64_t slots;       // workspace slots (each HPW heads x (D + 2) floats)
@@ -36,7 +37,9 @@ Plan make_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_
         max_context_len < 0 || partition_size < 0 || partition_size % PA_BLOCK_SIZE != 0 ||
         partition_size > kMaxPartition)
         return pl;
-    pl.hpw = pa::heads_per_workgroup(num_heads / num_kv_heads);
+    const pa::HeadGrouping hg = pa::head_grouping(num_heads / num_kv_heads);
+    pl.hpw = hg.hpw;
+    pl.mfma = hg.mfma;
     pl.groups = num_heads / pl.hpw;
     const int64_t seq_groups = (int64_t)num_seqs * pl.groups;
     const int64_t max_blocks = (max_context_len + PA_BLOCK_SIZE - 1) / PA_BLOCK_SIZE;
@@ -150,7 +153,7 @@ pa_status pa_decode(void* out, const void* query, const void* key_cache, const v
     if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
     if (!aligned(out, 16) || !aligned(query, 16) || !aligned(key_cache, 16) || !aligned(value_cache, 16) ||
         !aligned(block_tables, 4) || !aligned(context_lens, 4) || (need > 0 && !aligned(workspace, 16)) ||
-        (fp8 && (!aligned(k_scale, 4) || !aligned(v_scale, 4))))
+        (fp8 && (!aligned(k_scale, 16) || !aligned(v_scale, 16))))
         return PA_ERR_ALIGN;
 
     pa::DecodeParams p{};
@@ -175,9 +178,11 @@ pa_status pa_decode(void* out, const void* query, const void* key_cache, const v
     p.NP = (int32_t)pl.np;
     p.part_blocks = (int32_t)(pl.part / PA_BLOCK_SIZE);
     p.groups = (int32_t)pl.groups;
+    p.hpw = (int32_t)pl.hpw;
+    p.mfma = pl.mfma ? 1 : 0;
     p.num_waves = (int32_t)pl.waves;
     p.scale_log2 = scale * 1.4426950408889634f;
-    return from_hip(pa::launch_decode(p, head_dim, q_dtype, cache_dtype, (int)pl.hpw, (hipStream_t)stream));
+    return from_hip(pa::launch_decode(p, head_dim, q_dtype, cache_dtype, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -128,12 +128,14 @@ __device__ int seq_start(const DecodeParams& p, int lane, int b) {
     return carry;
 }
 
-// One segment: blocks [jb, je) of sequence b (nblk blocks, L tokens), head group hg.
-// Writes the output rows when the segment is the whole sequence, else the partial
-// for workspace slot `slot` (HPW consecutive heads per slot).
+// VALU path (head groups of 1, 2, 4 or 8 query heads).  One segment: blocks [jb, je) of
+// sequence b (nblk blocks, L tokens), head group hg.  Writes the output rows when the
+// segment is the whole sequence, else the partial for workspace slot `slot` (HPW
+// consecutive heads per slot).
 template <typename QT, typename CT, int D, int HPW>
-__device__ __forceinline__ void run_segment(const DecodeParams& p, int lane, int b, int hg, int jb, int je,
-                                            int nblk, int L, int64_t slot) {
+struct ValuSegment {
+static __device__ __forceinline__ void run(const DecodeParams& p, int lane, int b, int hg, int jb, int je,
+                                           int nblk, int L, int64_t slot) {
     using Ly = Layout<CT, D>;
     constexpr int EB = Ly::EB, EPL = Ly::EPL, TPL = Ly::TPL, ROWS = Ly::ROWS, LPB = Ly::LPB;
     constexpr bool kFp8 = EB == 1;
@@ -375,8 +377,251 @@ __device__ __forceinline__ void run_segment(const DecodeParams& p, int lane, int
         }
     }
 }
+};
 
-template <typename QT, typename CT, int D, int HPW>
+// Matrix-core path for head groups of 3..16 query heads sharing one KV head (rows of
+// a 16x16 tile; unused rows carry zero queries).  Per 16-token block:
+//   S^T[token][head] = K[token][:] . Q[head][:]     16x16x32 MFMAs over the head dim;
+//       K is the A operand straight from HBM (lane l: token l%16), Q the B operand.
+//   online softmax per head on S^T: lane l holds tokens 4(l/16)..+3 of head l%16, which is
+//       also the A-operand layout of P in the next product.
+//   O[head][d] += P[head][token] . V[token][d]     16x16x16 MFMAs, one per 16 columns;
+//       P is split into two operand-type terms (hi + lo) so that it keeps ~16 more bits
+//       than one 16-bit rounding; V goes through a per-wave LDS tile (row padded by 16
+//       bytes so the four token groups of a read hit disjoint banks) to reach the B-operand
+//       layout (lane l: column l%16, tokens 4(l/16)..+3).
+// FP8 caches are widened to the query's 16-bit type (exactly) before the products; the
+// per-token scales multiply the scores and P.
+template <typename QT, typename CT, int D>
+struct MfmaSegment {
+    using M = QT;
+    static constexpr int EB = Storage<CT>::bytes;
+    static constexpr bool kFp8 = EB == 1;
+    static constexpr int KSTEPS = D / 32;          // 16x16x32 steps over the head dimension
+    static constexpr int NT = D / 16;              // 16-column output tiles
+    static constexpr int KLOADS = kFp8 ? KSTEPS / 2 : KSTEPS;   // 16-byte K loads per lane per block
+    static constexpr int VEPL = 16 / EB;           // V cache elements per lane per 16-byte load
+    static constexpr int TPLV = D / VEPL;          // lanes per V token row
+    static constexpr int ROWSV = kWave / TPLV;     // V token rows per wave-wide load
+    static constexpr int LPBV = kBlockSize / ROWSV;
+    static constexpr int ROWB = D * 2 + 16;        // LDS bytes per V token row (16-bit, padded)
+
+    // Head-dimension index of element i (< 8) of MFMA step s for lane group g.  Any
+    // mapping works as long as K and Q use the same one; these keep every lane's 16-byte
+    // loads contiguous (FP8: one 16-byte load feeds two steps).
+    static __device__ __forceinline__ int dk(int s, int g) {
+        return kFp8 ? 64 * (s / 2) + 16 * g + 8 * (s % 2) : 32 * s + 8 * g;
+    }
+
+    // Eight FP8 codes (two words) -> eight operand-type values (exact).
+    static __device__ __forceinline__ uint4 widen8(uint32_t w0, uint32_t w1) {
+        float f[8];
+        unpack4_fp8(w0, f);
+        unpack4_fp8(w1, f + 4);
+        return uint4{Mma<M>::pack_rtz(f[0], f[1]), Mma<M>::pack_rtz(f[2], f[3]), Mma<M>::pack_rtz(f[4], f[5]),
+                     Mma<M>::pack_rtz(f[6], f[7])};
+    }
+
+    static __device__ __forceinline__ void run(const DecodeParams& p, int lane, int b, int hg, int jb, int je,
+                                               int nblk, int L, int64_t slot) {
+        __shared__ __align__(16) char lds_all[kWaves][kBlockSize * ROWB];
+        char* lds = lds_all[threadIdx.x / kWave];
+        const int G = p.hpw;
+        const int h0 = hg * G;
+        const int hk = h0 / (p.Hq / p.Hkv);
+        const int t16 = lane & 15;
+        const int g = lane >> 4;
+        const int vrow = lane / TPLV;
+        const int vchunk = lane % TPLV;
+
+        const int32_t* table = p.block_tables + (int64_t)b * p.max_blocks;
+        auto table_chunk = [&](int jbase) {
+            const int j = jbase + lane;
+            return j < p.max_blocks ? table[j] : -1;
+        };
+        int tbl = table_chunk(jb);
+
+        // Q as the B operand: lane l holds Q[head l%16][dk(s, l/16) + i]; zero past the group.
+        uint4 qb[KSTEPS];
+        {
+            const bool hv = t16 < G;
+            const uint16_t* qrow = (const uint16_t*)p.query + ((int64_t)b * p.Hq + h0 + (hv ? t16 : 0)) * D;
+#pragma unroll
+            for (int s = 0; s < KSTEPS; ++s) qb[s] = hv ? *(const uint4*)(qrow + dk(s, g)) : uint4{0u, 0u, 0u, 0u};
+        }
+
+        f32x4_t O[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) O[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        float m = kNegInf;      // running max of head t16 (log2 units)
+        float lsum = 0.0f;      // this lane's share of the running sum of head t16
+
+        const int64_t tok_bytes = (int64_t)p.Hkv * D * EB;
+        const int64_t blk_bytes = tok_bytes * kBlockSize;
+        const uint32_t k_off = (uint32_t)(t16 * tok_bytes + (int64_t)hk * D * EB) + 16 * g;
+        const uint32_t v_off = (uint32_t)(vrow * tok_bytes + (int64_t)hk * D * EB + vchunk * 16);
+        const uint32_t v_step = (uint32_t)(ROWSV * tok_bytes);
+        const char* kbase = (const char*)p.key_cache;
+        const char* vbase = (const char*)p.value_cache;
+
+        auto issue = [&](int j, int jbase, uint4 (&kr)[KLOADS], uint4 (&vr)[LPBV], float4& ks, float4& vs) {
+            const int phys = __builtin_amdgcn_readlane(tbl, j - jbase);
+            const bool ok = phys >= 0 && phys < p.num_blocks;
+            const int64_t pb = ok ? phys : 0;
+            const char* kb = kbase + pb * blk_bytes;
+            const char* vb = vbase + pb * blk_bytes;
+            // K: lane l reads 16 bytes of token l%16 (16-bit: step s at byte 64 s + 16 g;
+            // FP8: steps 2c, 2c+1 at byte 64 c + 16 g).
+#pragma unroll
+            for (int c = 0; c < KLOADS; ++c) kr[c] = *(const uint4*)(kb + k_off + 64 * c);
+#pragma unroll
+            for (int i = 0; i < LPBV; ++i) vr[i] = *(const uint4*)(vb + v_off + i * v_step);
+            if constexpr (kFp8) {
+                ks = *(const float4*)(p.k_scale + pb * kBlockSize + 4 * g);
+                vs = *(const float4*)(p.v_scale + pb * kBlockSize + 4 * g);
+            }
+            return ok;
+        };
+
+        auto consume = [&](int j, const uint4 (&kr)[KLOADS], const uint4 (&vr)[LPBV], const float4& ks,
+                           const float4& vs) {
+            // S^T for the block's 16 tokens x 16 head rows.
+            f32x4_t S = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            if constexpr (!kFp8) {
+#pragma unroll
+                for (int s = 0; s < KSTEPS; ++s) S = Mma<M>::k32(kr[s], qb[s], S);
+            } else {
+#pragma unroll
+                for (int c = 0; c < KLOADS; ++c) {
+                    S = Mma<M>::k32(widen8(kr[c].x, kr[c].y), qb[2 * c], S);
+                    S = Mma<M>::k32(widen8(kr[c].z, kr[c].w), qb[2 * c + 1], S);
+                }
+            }
+            const float ksc[4] = {ks.x, ks.y, ks.z, ks.w};
+            const float vsc[4] = {vs.x, vs.y, vs.z, vs.w};
+            float sc[4];
+            bool valid[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                valid[r] = j * kBlockSize + 4 * g + r < L;
+                const float f = kFp8 ? p.scale_log2 * ksc[r] : p.scale_log2;
+                sc[r] = valid[r] ? S[r] * f : kNegInf;
+            }
+            float mb = __builtin_fmaxf(__builtin_fmaxf(sc[0], sc[1]), __builtin_fmaxf(sc[2], sc[3]));
+            mb = __builtin_fmaxf(mb, __shfl_xor(mb, 16));
+            mb = __builtin_fmaxf(mb, __shfl_xor(mb, 32));
+            const float mn = __builtin_fmaxf(m, mb);
+            const float ms = (mn == kNegInf) ? 0.0f : mn;
+            const float alpha = fast_exp2(m - ms);
+            m = mn;
+            float pr[4];
+            float psum = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                pr[r] = fast_exp2(sc[r] - ms);
+                psum += pr[r];
+                if constexpr (kFp8) pr[r] = valid[r] ? pr[r] * vsc[r] : 0.0f;
+            }
+            lsum = lsum * alpha + psum;
+            // Rescale the output rows (heads 4g + r) when some running max moved.
+            if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float ar = __shfl(alpha, 4 * g + r);
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) O[t][r] *= ar;
+                }
+            }
+
+            // V rows of the block into this wave's LDS tile as operand-type values; rows past
+            // the context are written as zeros (P is zero there, and 0 * NaN would not be).
+#pragma unroll
+            for (int i = 0; i < LPBV; ++i) {
+                const int row = i * ROWSV + vrow;
+                const bool vv = j * kBlockSize + row < L;
+                const uint4 w = vv ? vr[i] : uint4{0u, 0u, 0u, 0u};
+                if constexpr (!kFp8) {
+                    *(uint4*)(lds + row * ROWB + vchunk * 16) = w;
+                } else {
+                    *(uint4*)(lds + row * ROWB + vchunk * 32) = widen8(w.x, w.y);
+                    *(uint4*)(lds + row * ROWB + vchunk * 32 + 16) = widen8(w.z, w.w);
+                }
+            }
+
+            // P = hi + lo in the operand type (A operand: head l%16, tokens 4g..4g+3).
+            const uint32_t h01 = Mma<M>::pack_rtz(pr[0], pr[1]);
+            const uint32_t h23 = Mma<M>::pack_rtz(pr[2], pr[3]);
+            const float2_t f01 = unpack2(M{}, h01);
+            const float2_t f23 = unpack2(M{}, h23);
+            const uint2 a_hi = uint2{h01, h23};
+            const uint2 a_lo = uint2{Mma<M>::pack_rtz(pr[0] - f01.x, pr[1] - f01.y),
+                                     Mma<M>::pack_rtz(pr[2] - f23.x, pr[3] - f23.y)};
+            const uint16_t* vt = (const uint16_t*)lds;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const int col = 16 * t + t16;
+                const uint32_t e0 = vt[((4 * g + 0) * ROWB) / 2 + col];
+                const uint32_t e1 = vt[((4 * g + 1) * ROWB) / 2 + col];
+                const uint32_t e2 = vt[((4 * g + 2) * ROWB) / 2 + col];
+                const uint32_t e3 = vt[((4 * g + 3) * ROWB) / 2 + col];
+                const uint2 bt = uint2{e0 | (e1 << 16), e2 | (e3 << 16)};
+                O[t] = Mma<M>::k16(a_hi, bt, O[t]);
+                O[t] = Mma<M>::k16(a_lo, bt, O[t]);
+            }
+        };
+
+        uint4 kA[KLOADS], vA[LPBV], kB[KLOADS], vB[LPBV];
+        float4 ksA, vsA, ksB, vsB;
+        for (int jc = jb; jc < je; jc += kWave) {
+            if (jc != jb) tbl = table_chunk(jc);
+            const int jend = min(je, jc + kWave);
+            int j = jc;
+            bool okA = issue(j, jc, kA, vA, ksA, vsA);
+            while (j + 2 < jend) {
+                const bool okB = issue(j + 1, jc, kB, vB, ksB, vsB);
+                if (okA) consume(j, kA, vA, ksA, vsA);
+                okA = issue(j + 2, jc, kA, vA, ksA, vsA);
+                if (okB) consume(j + 1, kB, vB, ksB, vsB);
+                j += 2;
+            }
+            if (j + 1 < jend) {
+                const bool okB = issue(j + 1, jc, kB, vB, ksB, vsB);
+                if (okA) consume(j, kA, vA, ksA, vsA);
+                if (okB) consume(j + 1, kB, vB, ksB, vsB);
+            } else if (okA) {
+                consume(j, kA, vA, ksA, vsA);
+            }
+        }
+
+        // Totals per head (lane groups hold disjoint tokens), then per output row 4g + r.
+        float ltot = lsum + __shfl_xor(lsum, 16);
+        ltot += __shfl_xor(ltot, 32);
+        const bool whole = jb == 0 && je == nblk;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int head = 4 * g + r;
+            const float lr = __shfl(ltot, head);
+            if (head >= G) continue;
+            if (whole) {
+                const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
+                uint16_t* orow = (uint16_t*)p.out + ((int64_t)b * p.Hq + h0 + head) * D;
+#pragma unroll
+                for (int t = 0; t < NT; ++t) orow[16 * t + t16] = to_bits(QT{}, O[t][r] * inv);
+            } else {
+                float* arow = p.ws_acc + (slot * G + head) * D;
+#pragma unroll
+                for (int t = 0; t < NT; ++t) arow[16 * t + t16] = O[t][r];
+            }
+        }
+        if (!whole && g == 0 && t16 < G) {
+            p.ws_ml[(slot * G + t16) * 2] = m;
+            p.ws_ml[(slot * G + t16) * 2 + 1] = ltot;
+        }
+    }
+};
+
+
+template <typename Segment>
 __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeParams p) {
     const int lane = threadIdx.x & (kWave - 1);
     const int w = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -393,7 +638,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeParams p) 
         const int jb = part * p.part_blocks;
         if (jb >= nblk && !(part == 0 && nblk == 0)) return;   // L == 0: partition 0 writes zeros
         const int je = min(nblk, jb + p.part_blocks);
-        run_segment<QT, CT, D, HPW>(p, lane, b, hg, jb, je, nblk, L, (int64_t)s * p.NP + part);
+        Segment::run(p, lane, b, hg, jb, je, nblk, L, (int64_t)s * p.NP + part);
         return;
     }
 
@@ -409,7 +654,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeParams p) 
         const int jb = off % sp.nblk;
         const int je = min(sp.nblk, jb + (pos_end - pos));
         const int s = sp.b * p.groups + hg;
-        run_segment<QT, CT, D, HPW>(p, lane, sp.b, hg, jb, je, sp.nblk, seq_len(p, sp.b), (int64_t)w + s);
+        Segment::run(p, lane, sp.b, hg, jb, je, sp.nblk, seq_len(p, sp.b), (int64_t)w + s);
         pos += je - jb;
     }
 }
@@ -417,13 +662,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeParams p) 
 // Merge of the partials of one (sequence, head group): for each head,
 // out = sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k over its segments in
 // ascending token order.  Also writes the zero rows of empty sequences in the
-// balanced split (no segment covers them).
-template <typename QT, int D, int HPW>
-__global__ __launch_bounds__(kWave * (HPW < 4 ? HPW : 4)) void decode_merge_kernel(const DecodeParams p) {
+// balanced split (no segment covers them).  Up to 4 waves, each taking every
+// 4th head of the group.
+template <typename QT, int D>
+__global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeParams p) {
     constexpr int EPT = D / kWave;
-    constexpr int NW = HPW < 4 ? HPW : 4;   // waves, each merging heads wave, wave + NW, ...
+    const int hpw = p.hpw;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int nw = blockDim.x / kWave;
     const int s = blockIdx.x;
     const int hg = s % p.groups;
     const int b = s / p.groups;
@@ -451,10 +698,10 @@ __global__ __launch_bounds__(kWave * (HPW < 4 ? HPW : 4)) void decode_merge_kern
         }
     }
 
-    for (int h = wave; h < HPW; h += NW) {
-        const int64_t base = first * HPW + h;   // slot k of this head: (first + k) * HPW + h
+    for (int h = wave; h < hpw; h += nw) {
+        const int64_t base = first * hpw + h;   // slot k of this head: (first + k) * hpw + h
         float M = kNegInf;
-        for (int k = 0; k < count; ++k) M = __builtin_fmaxf(M, p.ws_ml[(base + (int64_t)k * HPW) * 2]);
+        for (int k = 0; k < count; ++k) M = __builtin_fmaxf(M, p.ws_ml[(base + (int64_t)k * hpw) * 2]);
         const float ms = (M == kNegInf) ? 0.0f : M;
         float num[EPT];
 #pragma unroll
@@ -462,13 +709,13 @@ __global__ __launch_bounds__(kWave * (HPW < 4 ? HPW : 4)) void decode_merge_kern
         float den = 0.0f;
 #pragma unroll 4
         for (int k = 0; k < count; ++k) {
-            const int64_t hs = base + (int64_t)k * HPW;
+            const int64_t hs = base + (int64_t)k * hpw;
             const float f = fast_exp2(p.ws_ml[hs * 2] - ms);
             den = __builtin_fmaf(f, p.ws_ml[hs * 2 + 1], den);
 #pragma unroll
             for (int e = 0; e < EPT; ++e) num[e] = __builtin_fmaf(f, p.ws_acc[hs * D + e * kWave + lane], num[e]);
         }
-        const int64_t out_row = (int64_t)b * p.Hq + hg * HPW + h;
+        const int64_t out_row = (int64_t)b * p.Hq + hg * hpw + h;
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {
             const float o = den > 0.0f ? num[e] / den : 0.0f;
@@ -477,51 +724,56 @@ __global__ __launch_bounds__(kWave * (HPW < 4 ? HPW : 4)) void decode_merge_kern
     }
 }
 
-template <typename QT, typename CT, int D, int HPW>
+template <typename QT, int D, typename Segment>
 hipError_t run(const DecodeParams& p, hipStream_t stream) {
     const int64_t grid = ((int64_t)p.num_waves + kWaves - 1) / kWaves;
-    hipLaunchKernelGGL((decode_kernel<QT, CT, D, HPW>), dim3((uint32_t)grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((decode_kernel<Segment>), dim3((uint32_t)grid), dim3(kThreads), 0, stream, p);
     if (p.balanced || p.NP > 1) {
-        hipLaunchKernelGGL((decode_merge_kernel<QT, D, HPW>), dim3((uint32_t)((int64_t)p.B * p.groups)),
-                           dim3(kWave * (HPW < 4 ? HPW : 4)), 0, stream, p);
+        const int waves = p.hpw < 4 ? p.hpw : 4;
+        hipLaunchKernelGGL((decode_merge_kernel<QT, D>), dim3((uint32_t)((int64_t)p.B * p.groups)),
+                           dim3(kWave * waves), 0, stream, p);
     }
     return hipGetLastError();
 }
 
 template <typename QT, typename CT, int D>
-hipError_t run_hpw(const DecodeParams& p, int hpw, hipStream_t s) {
-    switch (hpw) {
-        case 1: return run<QT, CT, D, 1>(p, s);
-        case 2: return run<QT, CT, D, 2>(p, s);
-        case 4: return run<QT, CT, D, 4>(p, s);
-        case 8: return run<QT, CT, D, 8>(p, s);
+hipError_t run_path(const DecodeParams& p, hipStream_t s) {
+    if (p.mfma) return run<QT, D, MfmaSegment<QT, CT, D>>(p, s);
+    switch (p.hpw) {
+        case 1: return run<QT, D, ValuSegment<QT, CT, D, 1>>(p, s);
+        case 2: return run<QT, D, ValuSegment<QT, CT, D, 2>>(p, s);
+        case 4: return run<QT, D, ValuSegment<QT, CT, D, 4>>(p, s);
+        case 8: return run<QT, D, ValuSegment<QT, CT, D, 8>>(p, s);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <typename QT, typename CT>
-hipError_t run_d(const DecodeParams& p, int d, int hpw, hipStream_t s) {
+hipError_t run_d(const DecodeParams& p, int d, hipStream_t s) {
     switch (d) {
-        case 64: return run_hpw<QT, CT, 64>(p, hpw, s);
-        case 128: return run_hpw<QT, CT, 128>(p, hpw, s);
+        case 64: return run_path<QT, CT, 64>(p, s);
+        case 128: return run_path<QT, CT, 128>(p, s);
         default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
-int heads_per_workgroup(int group) {
+HeadGrouping head_grouping(int group) {
+    // Groups of 3 to 16 heads (or multiples of 16) go to the matrix cores, padded to 16
+    // rows; smaller groups stay on the VALU path.
+    if (group % 16 == 0) return {16, true};
+    if (group >= 3 && group <= 16) return {group, true};
     for (int h = 8; h > 1; h >>= 1)
-        if (group % h == 0) return h;
-    return 1;
+        if (group % h == 0) return {h, false};
+    return {1, false};
 }
 
-hipError_t launch_decode(const DecodeParams& p, int head_dim, int q_kind, int cache_kind, int hpw,
-                         hipStream_t stream) {
-    if (q_kind == kF16 && cache_kind == kF16) return run_d<F16, F16>(p, head_dim, hpw, stream);
-    if (q_kind == kBF16 && cache_kind == kBF16) return run_d<BF16, BF16>(p, head_dim, hpw, stream);
-    if (q_kind == kF16 && cache_kind == kFP8) return run_d<F16, FP8>(p, head_dim, hpw, stream);
-    if (q_kind == kBF16 && cache_kind == kFP8) return run_d<BF16, FP8>(p, head_dim, hpw, stream);
+hipError_t launch_decode(const DecodeParams& p, int head_dim, int q_kind, int cache_kind, hipStream_t stream) {
+    if (q_kind == kF16 && cache_kind == kF16) return run_d<F16, F16>(p, head_dim, stream);
+    if (q_kind == kBF16 && cache_kind == kBF16) return run_d<BF16, BF16>(p, head_dim, stream);
+    if (q_kind == kF16 && cache_kind == kFP8) return run_d<F16, FP8>(p, head_dim, stream);
+    if (q_kind == kBF16 && cache_kind == kFP8) return run_d<BF16, FP8>(p, head_dim, stream);
     return hipErrorInvalidValue;
 }
 

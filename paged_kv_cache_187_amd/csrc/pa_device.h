@@ -116,4 +116,50 @@ __device__ __forceinline__ uint32_t e4m3_encode(float y) {
     return sign | mag;
 }
 
+// ---------------------------------------------------------------------------
+// 16x16 matrix-core tiles (fp32 accumulate) in operand type M (F16 or BF16).
+// Lane layouts (wave64, checked on gfx950): for the 16x16x32 shape lane l holds
+// A[l%16][8*(l/16)+i] and B[8*(l/16)+i][l%16], i < 8; for 16x16x16 the same with
+// 4*(l/16)+i, i < 4; the fp32 result holds C[4*(l/16)+r][l%16], r < 4.
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <typename M>
+struct Mma;
+
+template <>
+struct Mma<BF16> {
+    static __device__ __forceinline__ f32x4_t k32(uint4 a, uint4 b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                      c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x4_t k16(uint2 a, uint2 b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a),
+                                                         __builtin_bit_cast(s16x4_t, b), c, 0, 0, 0);
+    }
+    // Two floats -> one packed pair, rounded toward zero (exact for values the type holds).
+    static __device__ __forceinline__ uint32_t pack_rtz(float lo, float hi) {
+        return (__float_as_uint(hi) & 0xFFFF0000u) | (__float_as_uint(lo) >> 16);
+    }
+};
+
+template <>
+struct Mma<F16> {
+    static __device__ __forceinline__ f32x4_t k32(uint4 a, uint4 b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                     0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x4_t k16(uint2 a, uint2 b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a), __builtin_bit_cast(f16x4_t, b), c,
+                                                    0, 0, 0);
+    }
+    static __device__ __forceinline__ uint32_t pack_rtz(float lo, float hi) {
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+    }
+};
+
 }  // namespace pa

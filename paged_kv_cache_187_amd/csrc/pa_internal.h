@@ -26,7 +26,9 @@ struct DecodeParams {
     int32_t balanced;          // 1: equal (sequence, head group, block) ranges per wave
     int32_t NP;                // fixed split: partitions per sequence in the grid
     int32_t part_blocks;       // fixed split: partition length in 16-token blocks
-    int32_t groups;            // head groups per sequence = Hq / heads per wave
+    int32_t groups;            // head groups per sequence = Hq / hpw
+    int32_t hpw;               // query heads per wave (all share one KV head)
+    int32_t mfma;              // 1: matrix-core path (hpw <= 16 rows of a 16x16 tile)
     int32_t num_waves;         // waves in the grid
     float scale_log2;          // softmax scale * log2(e)
 };
@@ -39,11 +41,14 @@ hipError_t launch_append_fp8(const void* key, const void* value, void* key_cache
                              float* k_scale, float* v_scale, const int64_t* slots, int64_t num_tokens,
                              int32_t row_elems, int64_t num_slots, int src_kind, hipStream_t stream);
 
-// Query heads of one KV head handled together by one wave (largest of 8, 4,
-// 2, 1 dividing the group size).
-int heads_per_workgroup(int group);
+// Query heads of one KV head handled together by one wave, and whether that
+// wave uses the matrix cores.
+struct HeadGrouping {
+    int hpw;
+    bool mfma;
+};
+HeadGrouping head_grouping(int group);
 
-hipError_t launch_decode(const DecodeParams& p, int head_dim, int q_kind, int cache_kind, int heads_per_wg,
-                         hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, int head_dim, int q_kind, int cache_kind, hipStream_t stream);
 
 }  // namespace pa
