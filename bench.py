@@ -271,7 +271,7 @@ def main():
             "tokens_in_cache": int(main_r["w"].lens_np.sum()),
         },
         "roofline": {
-            "kernel": "pa_decode (decode_partition_kernel + decode_reduce_kernel)",
+            "kernel": "pa_decode (decode_kernel + decode_merge_kernel)",
             "bound": "hbm",
             "achieved": s["effective_GBs"],
             "peak": HBM_PEAK_GBS,

@@ -128,12 +128,44 @@ __device__ int seq_start(const DecodeParams& p, int lane, int b) {
     return carry;
 }
 
+// Streams logical blocks [jb, je) of one sequence through NB register buffers:
+// consume(j, buf) runs for every block in order while the loads of the next NB-1
+// blocks are in flight.  Every issue is unconditional (the compiler can then count
+// the loads and wait exactly for the oldest buffer); issues past the end re-read
+// the last block, which is still in L2, and are never consumed.  The page table is
+// read 64 ids at a time, one per lane (`tbl`, refreshed by table_chunk).
+template <int NB, typename Buf, typename TableFn, typename IssueFn, typename ConsumeFn>
+__device__ __forceinline__ void stream_blocks(int jb, int je, int& tbl, TableFn table_chunk, IssueFn issue,
+                                              ConsumeFn consume) {
+    Buf buf[NB];
+    bool ok[NB];
+    for (int jc = jb; jc < je; jc += kWave) {
+        if (jc != jb) tbl = table_chunk(jc);
+        const int jend = min(je, jc + kWave);
+        const int last = jend - 1;
+#pragma unroll
+        for (int k = 0; k < NB - 1; ++k) ok[k] = issue(min(jc + k, last), jc, buf[k]);
+        for (int j = jc; j < jend; j += NB) {
+#pragma unroll
+            for (int k = 0; k < NB; ++k) {
+                const int nk = (k + NB - 1) % NB;
+                ok[nk] = issue(min(j + k + NB - 1, last), jc, buf[nk]);
+                if (j + k < jend && ok[k]) consume(j + k, buf[k]);
+            }
+        }
+    }
+}
+
 // VALU path (head groups of 1, 2, 4 or 8 query heads).  One segment: blocks [jb, je) of
 // sequence b (nblk blocks, L tokens), head group hg.  Writes the output rows when the
 // segment is the whole sequence, else the partial for workspace slot `slot` (HPW
 // consecutive heads per slot).
-template <typename QT, typename CT, int D, int HPW>
+template <typename QT, typename CT, int D, int HPW, int NB>
 struct ValuSegment {
+struct Buf {
+    uint4 k[Layout<CT, D>::LPB], v[Layout<CT, D>::LPB];
+    float ks[Layout<CT, D>::LPB], vs[Layout<CT, D>::LPB];
+};
 static __device__ __forceinline__ void run(const DecodeParams& p, int lane, int b, int hg, int jb, int je,
                                            int nblk, int L, int64_t slot) {
     using Ly = Layout<CT, D>;
@@ -200,7 +232,11 @@ static __device__ __forceinline__ void run(const DecodeParams& p, int lane, int 
     // compiler can count them exactly (the consumer of the older buffer then waits only for
     // its own loads); an out-of-range physical id reads block 0 instead and the function
     // returns false so that the block is skipped.
-    auto issue = [&](int j, int jbase, uint4 (&kr)[LPB], uint4 (&vr)[LPB], float (&ksc)[LPB], float (&vsc)[LPB]) {
+    auto issue = [&](int j, int jbase, Buf& bf) {
+        uint4(&kr)[LPB] = bf.k;
+        uint4(&vr)[LPB] = bf.v;
+        float(&ksc)[LPB] = bf.ks;
+        float(&vsc)[LPB] = bf.vs;
         const int phys = __builtin_amdgcn_readlane(tbl, j - jbase);
         const bool ok = phys >= 0 && phys < p.num_blocks;
         const int64_t pb = ok ? phys : 0;
@@ -221,8 +257,11 @@ static __device__ __forceinline__ void run(const DecodeParams& p, int lane, int 
     };
 
     // Online-softmax update with the LPB tokens this row holds of block j.
-    auto consume = [&](int j, const uint4 (&kr)[LPB], const uint4 (&vr)[LPB], const float (&ksc)[LPB],
-                       const float (&vsc)[LPB]) {
+    auto consume = [&](int j, const Buf& bf) {
+        const uint4(&kr)[LPB] = bf.k;
+        const uint4(&vr)[LPB] = bf.v;
+        const float(&ksc)[LPB] = bf.ks;
+        const float(&vsc)[LPB] = bf.vs;
         bool valid[LPB];
 #pragma unroll
         for (int i = 0; i < LPB; ++i) valid[i] = j * kBlockSize + i * ROWS + row < L;
@@ -306,30 +345,7 @@ static __device__ __forceinline__ void run(const DecodeParams& p, int lane, int 
         }
     };
 
-    // Two register buffers: the loads of block j+1 are in flight while block j is consumed.
-    // The page table is walked in chunks of 64 blocks (one id per lane).
-    uint4 kA[LPB], vA[LPB], kB[LPB], vB[LPB];
-    float ksA[LPB], vsA[LPB], ksB[LPB], vsB[LPB];
-    for (int jc = jb; jc < je; jc += kWave) {
-        if (jc != jb) tbl = table_chunk(jc);
-        const int jend = min(je, jc + kWave);
-        int j = jc;
-        bool okA = issue(j, jc, kA, vA, ksA, vsA);
-        while (j + 2 < jend) {
-            const bool okB = issue(j + 1, jc, kB, vB, ksB, vsB);
-            if (okA) consume(j, kA, vA, ksA, vsA);
-            okA = issue(j + 2, jc, kA, vA, ksA, vsA);
-            if (okB) consume(j + 1, kB, vB, ksB, vsB);
-            j += 2;
-        }
-        if (j + 1 < jend) {
-            const bool okB = issue(j + 1, jc, kB, vB, ksB, vsB);
-            if (okA) consume(j, kA, vA, ksA, vsA);
-            if (okB) consume(j + 1, kB, vB, ksB, vsB);
-        } else if (okA) {
-            consume(j, kA, vA, ksA, vsA);
-        }
-    }
+    stream_blocks<NB, Buf>(jb, je, tbl, table_chunk, issue, consume);
 
     // Merge the ROWS row states (lanes with equal `chunk`); afterwards every row holds the
     // segment's result and the TPL lanes of row 0 write it.
@@ -392,7 +408,7 @@ static __device__ __forceinline__ void run(const DecodeParams& p, int lane, int 
 //       layout (lane l: column l%16, tokens 4(l/16)..+3).
 // FP8 caches are widened to the query's 16-bit type (exactly) before the products; the
 // per-token scales multiply the scores and P.
-template <typename QT, typename CT, int D>
+template <typename QT, typename CT, int D, int NB>
 struct MfmaSegment {
     using M = QT;
     static constexpr int EB = Storage<CT>::bytes;
@@ -405,6 +421,11 @@ struct MfmaSegment {
     static constexpr int ROWSV = kWave / TPLV;     // V token rows per wave-wide load
     static constexpr int LPBV = kBlockSize / ROWSV;
     static constexpr int ROWB = D * 2 + 16;        // LDS bytes per V token row (16-bit, padded)
+
+    struct Buf {
+        uint4 k[KLOADS], v[LPBV];
+        float4 ks, vs;
+    };
 
     // Head-dimension index of element i (< 8) of MFMA step s for lane group g.  Any
     // mapping works as long as K and Q use the same one; these keep every lane's 16-byte
@@ -464,7 +485,11 @@ struct MfmaSegment {
         const char* kbase = (const char*)p.key_cache;
         const char* vbase = (const char*)p.value_cache;
 
-        auto issue = [&](int j, int jbase, uint4 (&kr)[KLOADS], uint4 (&vr)[LPBV], float4& ks, float4& vs) {
+        auto issue = [&](int j, int jbase, Buf& bf) {
+            uint4(&kr)[KLOADS] = bf.k;
+            uint4(&vr)[LPBV] = bf.v;
+            float4& ks = bf.ks;
+            float4& vs = bf.vs;
             const int phys = __builtin_amdgcn_readlane(tbl, j - jbase);
             const bool ok = phys >= 0 && phys < p.num_blocks;
             const int64_t pb = ok ? phys : 0;
@@ -483,8 +508,11 @@ struct MfmaSegment {
             return ok;
         };
 
-        auto consume = [&](int j, const uint4 (&kr)[KLOADS], const uint4 (&vr)[LPBV], const float4& ks,
-                           const float4& vs) {
+        auto consume = [&](int j, const Buf& bf) {
+            const uint4(&kr)[KLOADS] = bf.k;
+            const uint4(&vr)[LPBV] = bf.v;
+            const float4& ks = bf.ks;
+            const float4& vs = bf.vs;
             // S^T for the block's 16 tokens x 16 head rows.
             f32x4_t S = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
             if constexpr (!kFp8) {
@@ -570,28 +598,7 @@ struct MfmaSegment {
             }
         };
 
-        uint4 kA[KLOADS], vA[LPBV], kB[KLOADS], vB[LPBV];
-        float4 ksA, vsA, ksB, vsB;
-        for (int jc = jb; jc < je; jc += kWave) {
-            if (jc != jb) tbl = table_chunk(jc);
-            const int jend = min(je, jc + kWave);
-            int j = jc;
-            bool okA = issue(j, jc, kA, vA, ksA, vsA);
-            while (j + 2 < jend) {
-                const bool okB = issue(j + 1, jc, kB, vB, ksB, vsB);
-                if (okA) consume(j, kA, vA, ksA, vsA);
-                okA = issue(j + 2, jc, kA, vA, ksA, vsA);
-                if (okB) consume(j + 1, kB, vB, ksB, vsB);
-                j += 2;
-            }
-            if (j + 1 < jend) {
-                const bool okB = issue(j + 1, jc, kB, vB, ksB, vsB);
-                if (okA) consume(j, kA, vA, ksA, vsA);
-                if (okB) consume(j + 1, kB, vB, ksB, vsB);
-            } else if (okA) {
-                consume(j, kA, vA, ksA, vsA);
-            }
-        }
+        stream_blocks<NB, Buf>(jb, je, tbl, table_chunk, issue, consume);
 
         // Totals per head (lane groups hold disjoint tokens), then per output row 4g + r.
         float ltot = lsum + __shfl_xor(lsum, 16);
@@ -736,14 +743,17 @@ hipError_t run(const DecodeParams& p, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// Two blocks in flight per wave: deeper rings measured no faster.
+constexpr int kRing = 2;
+
 template <typename QT, typename CT, int D>
 hipError_t run_path(const DecodeParams& p, hipStream_t s) {
-    if (p.mfma) return run<QT, D, MfmaSegment<QT, CT, D>>(p, s);
+    if (p.mfma) return run<QT, D, MfmaSegment<QT, CT, D, kRing>>(p, s);
     switch (p.hpw) {
-        case 1: return run<QT, D, ValuSegment<QT, CT, D, 1>>(p, s);
-        case 2: return run<QT, D, ValuSegment<QT, CT, D, 2>>(p, s);
-        case 4: return run<QT, D, ValuSegment<QT, CT, D, 4>>(p, s);
-        case 8: return run<QT, D, ValuSegment<QT, CT, D, 8>>(p, s);
+        case 1: return run<QT, D, ValuSegment<QT, CT, D, 1, kRing>>(p, s);
+        case 2: return run<QT, D, ValuSegment<QT, CT, D, 2, kRing>>(p, s);
+        case 4: return run<QT, D, ValuSegment<QT, CT, D, 4, kRing>>(p, s);
+        case 8: return run<QT, D, ValuSegment<QT, CT, D, 8, kRing>>(p, s);
         default: return hipErrorInvalidValue;
     }
 }
