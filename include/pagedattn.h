@@ -128,7 +128,8 @@ int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_heads, int32_t nu
  * i.e. fixed partitions with max_context_len <= partition_size).  The
  * workspace holds float32 partial results: per (slot, head of the group) a
  * V sum of head_dim floats, followed by all (max, sum of exponentials)
- * pairs.  Its contents need no initialisation and are scratch after the call.
+ * pairs.  Its contents need no initialisation and are scratch after the call;
+ * calls that share a workspace must not run concurrently.
  */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_context_len,

@@ -48,6 +48,7 @@ Plan make_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_
     if (pl.balanced) {
         const int64_t work = seq_groups * max_blocks;   // upper bound of (head group, block) pairs
         pl.waves = work < kBalancedWaves ? (work > 0 ? work : 1) : kBalancedWaves;
+        // a partial goes to slot range + (sequence, head group)
         pl.slots = pl.waves + seq_groups;
     } else {
         pl.part = partition_size;
@@ -165,8 +166,10 @@ pa_status pa_decode(void* out, const void* query, const void* key_cache, const v
     p.v_scale = fp8 ? v_scale : nullptr;
     p.block_tables = block_tables;
     p.context_lens = context_lens;
-    p.ws_acc = need > 0 ? (float*)workspace : nullptr;
-    p.ws_ml = need > 0 ? (float*)workspace + (size_t)pl.slots * pl.hpw * head_dim : nullptr;
+    if (need > 0) {
+        p.ws_acc = (float*)workspace;
+        p.ws_ml = p.ws_acc + (size_t)pl.slots * pl.hpw * head_dim;
+    }
     p.num_blocks = num_blocks;
     p.B = num_seqs;
     p.Hq = num_heads;

@@ -10,9 +10,10 @@
 // §4.1): the design goal is to keep enough 16-byte loads in flight, not to
 // use the matrix cores.
 //
-// Work split.  Every wave works alone (no LDS, no barriers) on segments: runs
-// of consecutive 16-token blocks of one (sequence, head group), a head group
-// being up to 8 query heads that share one KV head.  Two ways to cut the work:
+// Work split.  Every wave works alone (no barriers; the matrix-core path uses a
+// per-wave LDS tile) on segments: runs of consecutive 16-token blocks of one
+// (sequence, head group), a head group being the query heads of one KV head
+// that one wave serves.  Two ways to cut the work:
 //  * fixed partitions: wave = (sequence, head group, partition of P tokens);
 //  * balanced: the (sequence, head group, block) space is laid end to end and
 //    cut into equal ranges, one per wave, so long and short sequences cost
@@ -94,10 +95,33 @@ struct SeqPos {
     int nblk;    // blocks of this sequence
 };
 
+// Block counts of the sequences, read once per wave: lane b holds sequence b's
+// block count and exclusive block prefix when there are at most 64 sequences
+// (`single`); otherwise the lookups below walk the lengths 64 at a time.
+struct SeqTable {
+    int nb, start, total;
+    bool single;
+};
+
+__device__ SeqTable seq_table(const DecodeParams& p, int lane) {
+    SeqTable st;
+    st.single = p.B <= kWave;
+    st.nb = lane < p.B ? seq_blocks(p, lane) : 0;
+    const int incl = wave_incl_scan(st.nb, lane);
+    st.start = incl - st.nb;
+    st.total = st.single ? __builtin_amdgcn_readlane(incl, kWave - 1) : total_blocks(p, lane);
+    return st;
+}
+
 // The non-empty sequence holding balanced-order position pos, where the
 // position of (b, hg, j) is groups * start_b + hg * nblk_b + j and
 // 0 <= pos < groups * total_blocks.
-__device__ SeqPos locate(const DecodeParams& p, int lane, int pos) {
+__device__ SeqPos locate(const DecodeParams& p, const SeqTable& st, int lane, int pos) {
+    if (st.single) {
+        const uint64_t mask = __ballot(st.nb > 0 && p.groups * st.start <= pos);
+        const int lb = 63 - __builtin_clzll(mask);
+        return {lb, __builtin_amdgcn_readlane(st.start, lb), __builtin_amdgcn_readlane(st.nb, lb)};
+    }
     int carry = 0;
     for (int c = 0; c < p.B; c += kWave) {
         const int b = c + lane;
@@ -115,17 +139,38 @@ __device__ SeqPos locate(const DecodeParams& p, int lane, int pos) {
     return {0, 0, 0};
 }
 
-// Exclusive block prefix of sequence b.
-__device__ int seq_start(const DecodeParams& p, int lane, int b) {
+// Block count and exclusive block prefix of sequence b (b wave-uniform).
+__device__ SeqPos seq_entry(const DecodeParams& p, const SeqTable& st, int lane, int b) {
+    if (st.single) return {b, __builtin_amdgcn_readlane(st.start, b), __builtin_amdgcn_readlane(st.nb, b)};
     int carry = 0;
     for (int c = 0; c < p.B; c += kWave) {
         const int bb = c + lane;
         const int nb = bb < p.B ? seq_blocks(p, bb) : 0;
         const int incl = wave_incl_scan(nb, lane);
-        if (b < c + kWave) return carry + __builtin_amdgcn_readlane(incl - nb, b - c);
+        if (b < c + kWave)
+            return {b, carry + __builtin_amdgcn_readlane(incl - nb, b - c), __builtin_amdgcn_readlane(nb, b - c)};
         carry += __builtin_amdgcn_readlane(incl, kWave - 1);
     }
-    return carry;
+    return {b, carry, 0};
+}
+
+// Ranges of the balanced split: the T positions are cut into W equal ranges of
+// C = ceil(T / W) positions, range w running on wave w.  Range boundaries depend
+// only on the lengths and the launch shape; a partial goes to slot
+// range + (sequence, head group), which is unique because ranges and sequences
+// both advance with the position.
+struct Ranges {
+    int T, C;
+    __device__ int begin(int w) const { return min(T, w * C); }
+    __device__ int end(int w) const { return min(T, (w + 1) * C); }
+    __device__ int range_of(int pos) const { return pos / C; }
+};
+
+__device__ Ranges make_ranges(const DecodeParams& p, int T) {
+    Ranges r;
+    r.T = T;
+    r.C = T > 0 ? (T + p.num_waves - 1) / p.num_waves : 1;
+    return r;
 }
 
 // Streams logical blocks [jb, je) of one sequence through NB register buffers:
@@ -649,13 +694,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeParams p) 
         return;
     }
 
-    // Balanced: equal ranges of the (sequence, head group, block) order.
-    const int T = p.groups * total_blocks(p, lane);
-    const int C = (T + p.num_waves - 1) / p.num_waves;
-    int pos = w * C;
-    const int pos_end = min(T, pos + C);
+    // Balanced split: range w of the (sequence, head group, block) order.
+    const SeqTable st = seq_table(p, lane);
+    const Ranges rg = make_ranges(p, p.groups * st.total);
+    int pos = rg.begin(w);
+    const int pos_end = rg.end(w);
     while (pos < pos_end) {
-        const SeqPos sp = locate(p, lane, pos);
+        const SeqPos sp = locate(p, st, lane, pos);
         const int off = pos - p.groups * sp.start;
         const int hg = off / sp.nblk;
         const int jb = off % sp.nblk;
@@ -666,69 +711,132 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeParams p) 
     }
 }
 
-// Merge of the partials of one (sequence, head group): for each head,
-// out = sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k over its segments in
-// ascending token order.  Also writes the zero rows of empty sequences in the
-// balanced split (no segment covers them).  Up to 4 waves, each taking every
-// 4th head of the group.
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) x = __builtin_fmaxf(x, __shfl_xor(x, off));
+    return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) x += __shfl_xor(x, off);
+    return x;
+}
+
+// Merge of the partials of one (sequence, query head), one wave each:
+// out = sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k over the segments of its
+// head group in ascending token order (M = max_k m_k).  Lane k reads the (m, l)
+// pair of partial k, so all pairs arrive in one round; the V sums are then
+// folded in order k = 0, 1, ... with every lane holding D/64 columns.  Also
+// writes the zero rows of empty sequences in the balanced split (no segment
+// covers them).
 template <typename QT, int D>
 __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeParams p) {
     constexpr int EPT = D / kWave;
-    const int hpw = p.hpw;
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int nw = blockDim.x / kWave;
-    const int s = blockIdx.x;
-    const int hg = s % p.groups;
-    const int b = s / p.groups;
-    const int nblk = seq_blocks(p, b);
+    const int64_t row = (int64_t)blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    if (row >= (int64_t)p.B * p.Hq) return;
+    const int b = (int)(row / p.Hq);
+    const int h = (int)(row % p.Hq);
+    const int hg = h / p.hpw;
+    const int hh = h % p.hpw;
+    const int64_t s = (int64_t)b * p.groups + hg;
+    uint16_t* orow = (uint16_t*)p.out + row * D;
 
-    int64_t first, count;
+    int64_t first;
+    int count;
     if (!p.balanced) {
+        const int nblk = seq_blocks(p, b);
         const int n_part = (nblk + p.part_blocks - 1) / p.part_blocks;
         if (n_part <= 1) return;            // written by the one partition (zeros when L == 0)
-        first = (int64_t)s * p.NP;
+        first = s * p.NP;
         count = n_part;
     } else {
-        const int T = p.groups * total_blocks(p, lane);
-        const int C = (T + p.num_waves - 1) / p.num_waves;
-        const int pos0 = p.groups * seq_start(p, lane, b) + hg * nblk;
-        if (nblk > 0) {
-            const int w0 = pos0 / C;
-            const int w1 = (pos0 + nblk - 1) / C;
-            if (w0 == w1) return;           // one segment: written directly
-            first = (int64_t)w0 + s;
-            count = w1 - w0 + 1;
-        } else {
-            first = 0;
-            count = 0;
+        const SeqTable st = seq_table(p, lane);
+        const Ranges rg = make_ranges(p, p.groups * st.total);
+        const SeqPos e = seq_entry(p, st, lane, b);
+        if (e.nblk == 0) {
+#pragma unroll
+            for (int k = 0; k < EPT; ++k) orow[k * kWave + lane] = to_bits(QT{}, 0.0f);
+            return;
         }
+        const int pos0 = p.groups * e.start + hg * e.nblk;
+        const int t0 = rg.range_of(pos0);
+        const int t1 = rg.range_of(pos0 + e.nblk - 1);
+        if (t0 == t1) return;               // one segment: written directly
+        first = t0 + s;
+        count = t1 - t0 + 1;
     }
 
-    for (int h = wave; h < hpw; h += nw) {
-        const int64_t base = first * hpw + h;   // slot k of this head: (first + k) * hpw + h
-        float M = kNegInf;
-        for (int k = 0; k < count; ++k) M = __builtin_fmaxf(M, p.ws_ml[(base + (int64_t)k * hpw) * 2]);
-        const float ms = (M == kNegInf) ? 0.0f : M;
-        float num[EPT];
+    const int hpw = p.hpw;
+    const float* ml = p.ws_ml;
+    const float* acc = p.ws_acc + (first * hpw + hh) * D + lane;   // partial k at acc[k * hpw * D]
+    const int64_t kstride = (int64_t)hpw * D;
+
+    // The V sums of the first kPre partials are loaded together with the (m, l) pairs.
+    constexpr int kPre = 8;
+    float pre[kPre][EPT];
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) num[e] = 0.0f;
-        float den = 0.0f;
-#pragma unroll 4
-        for (int k = 0; k < count; ++k) {
-            const int64_t hs = base + (int64_t)k * hpw;
-            const float f = fast_exp2(p.ws_ml[hs * 2] - ms);
-            den = __builtin_fmaf(f, p.ws_ml[hs * 2 + 1], den);
+    for (int k = 0; k < kPre; ++k)
 #pragma unroll
-            for (int e = 0; e < EPT; ++e) num[e] = __builtin_fmaf(f, p.ws_acc[hs * D + e * kWave + lane], num[e]);
+        for (int e = 0; e < EPT; ++e) pre[k][e] = k < count ? acc[k * kstride + e * kWave] : 0.0f;
+
+    float m0 = kNegInf, l0 = 0.0f;          // this lane's pair of the first 64 partials
+    float M = kNegInf;
+    for (int k0 = 0; k0 < count; k0 += kWave) {
+        const int k = k0 + lane;
+        float mk = kNegInf, lk = 0.0f;
+        if (k < count) {
+            const int64_t hs = (first + k) * hpw + hh;
+            mk = ml[hs * 2];
+            lk = ml[hs * 2 + 1];
         }
-        const int64_t out_row = (int64_t)b * p.Hq + hg * hpw + h;
+        if (k0 == 0) {
+            m0 = mk;
+            l0 = lk;
+        }
+        M = __builtin_fmaxf(M, wave_max(mk));
+    }
+    const float ms = (M == kNegInf) ? 0.0f : M;
+
+    float num[EPT];
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) {
-            const float o = den > 0.0f ? num[e] / den : 0.0f;
-            ((uint16_t*)p.out)[out_row * D + e * kWave + lane] = to_bits(QT{}, o);
+    for (int e = 0; e < EPT; ++e) num[e] = 0.0f;
+    float den = 0.0f;
+    for (int k0 = 0; k0 < count; k0 += kWave) {
+        const int k = k0 + lane;
+        float mk = m0, lk = l0;
+        if (k0 > 0) {
+            mk = kNegInf;
+            lk = 0.0f;
+            if (k < count) {
+                const int64_t hs = (first + k) * hpw + hh;
+                mk = ml[hs * 2];
+                lk = ml[hs * 2 + 1];
+            }
+        }
+        const float f = k < count ? fast_exp2(mk - ms) : 0.0f;
+        den += wave_sum(f * lk);
+        const int n = min(kWave, count - k0);
+        int j = 0;
+        if (k0 == 0) {
+#pragma unroll
+            for (; j < kPre; ++j) {
+                if (j >= n) break;
+                const float fj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), j));
+#pragma unroll
+                for (int e = 0; e < EPT; ++e) num[e] = __builtin_fmaf(fj, pre[j][e], num[e]);
+            }
+        }
+#pragma unroll 8
+        for (; j < n; ++j) {
+            const float fj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), j));
+#pragma unroll
+            for (int e = 0; e < EPT; ++e) num[e] = __builtin_fmaf(fj, acc[(k0 + j) * kstride + e * kWave], num[e]);
         }
     }
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) orow[e * kWave + lane] = to_bits(QT{}, den > 0.0f ? num[e] / den : 0.0f);
 }
 
 template <typename QT, int D, typename Segment>
@@ -736,9 +844,9 @@ hipError_t run(const DecodeParams& p, hipStream_t stream) {
     const int64_t grid = ((int64_t)p.num_waves + kWaves - 1) / kWaves;
     hipLaunchKernelGGL((decode_kernel<Segment>), dim3((uint32_t)grid), dim3(kThreads), 0, stream, p);
     if (p.balanced || p.NP > 1) {
-        const int waves = p.hpw < 4 ? p.hpw : 4;
-        hipLaunchKernelGGL((decode_merge_kernel<QT, D>), dim3((uint32_t)((int64_t)p.B * p.groups)),
-                           dim3(kWave * waves), 0, stream, p);
+        const int64_t rows = (int64_t)p.B * p.Hq;   // one merge wave per (sequence, query head)
+        hipLaunchKernelGGL((decode_merge_kernel<QT, D>), dim3((uint32_t)((rows + kWaves - 1) / kWaves)),
+                           dim3(kThreads), 0, stream, p);
     }
     return hipGetLastError();
 }

@@ -62,9 +62,11 @@ def test_partition_and_workspace_sizes(lib):
     # 131072 / 512 = 256 partitions of (128 + 2) floats per (seq, head)
     assert pa.decode_workspace_bytes(8, 32, 32, 128, 131072, 512) == 8 * 32 * 256 * 130 * 4
     assert pa.decode_workspace_bytes(4, 4, 4, 64, 50, 512) == 0               # one partition: none
-    # balanced: one slot per wave plus one per (sequence, head group); GQA 8 heads per wave
-    n = pa.decode_workspace_bytes(64, 64, 8, 128, 4096, 0)
-    assert n > 0 and n % (8 * 130 * 4) == 0
+    # balanced: one slot per wave (2048) plus one per (sequence, head group); GQA group of 8
+    # heads per wave (64 sequences x 8 groups)
+    assert pa.decode_workspace_bytes(64, 64, 8, 128, 4096, 0) == (2048 + 64 * 8) * 8 * 130 * 4
+    # little work: one wave per (head group, block) pair at most
+    assert pa.decode_workspace_bytes(2, 4, 4, 64, 20, 0) == (16 + 8) * 66 * 4
     with pytest.raises(pa.PagedAttnError):
         pa.decode_workspace_bytes(4, 4, 4, 64, 50, 17)
 

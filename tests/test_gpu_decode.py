@@ -170,3 +170,35 @@ def test_long_context_sampled():
     got = out.cpu()
     for (b, h), ref in refs.items():
         assert_close(got[b, h], ref, cfg.cache_dtype, f"longctx b={b} h={h} L={w.lens_np[b]}")
+
+
+def test_balanced_split_more_than_64_sequences():
+    # 130 sequences (lengths walked 64 at a time), some empty, many ranges crossing sequences.
+    _say("balanced: 130 sequences, empty ones")
+    lens = tuple(int(x) for x in np.random.default_rng(11).integers(0, 400, size=130))
+    lens = (0, 0) + lens[2:]
+    cfg = _cfg(name="many", num_seqs=130, num_heads=2, num_kv_heads=2, head_dim=64, len_args=lens, seed=12)
+    _run_and_check(cfg, partition_size=0)
+
+
+@pytest.mark.parametrize("hq,hkv", [(16, 4), (8, 8)])
+def test_balanced_split_reused_workspace_repeats_bitwise(hq, hkv):
+    _say(f"balanced: reused workspace, repeat bitwise, Hq={hq} Hkv={hkv}")
+    lens = (3000, 1, 2047, 0, 1500, 900, 2500, 16)
+    cfg = _cfg(name="tiles", num_seqs=len(lens), num_heads=hq, num_kv_heads=hkv, len_args=lens,
+               q_dtype="bf16", cache_dtype="bf16", seed=13)
+    wh = synth.make_workload(cfg)
+    w = to_device(wh)
+    ws = pa.alloc_workspace(w.query, hkv, w.max_context_len, 0)
+    assert ws is not None
+    gpu_step(w)
+    outs = []
+    for _ in range(3):
+        out = torch.empty_like(w.query)
+        pa.pa_decode(out, w.query, w.key_cache, w.value_cache, w.block_tables, w.context_lens, cfg.scale,
+                     w.max_context_len, partition_size=0, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append(out)
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+    assert_close(outs[0], oracle_decode(wh, oracle_caches(wh)), "bf16", "tiles")
