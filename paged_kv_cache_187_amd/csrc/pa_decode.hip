@@ -441,35 +441,54 @@ static __device__ __forceinline__ void run(const DecodeParams& p, int lane, int 
 };
 
 // Matrix-core path for head groups of 3..16 query heads sharing one KV head (rows of
-// a 16x16 tile; unused rows carry zero queries).  Per 16-token block:
-//   S^T[token][head] = K[token][:] . Q[head][:]     16x16x32 MFMAs over the head dim;
-//       K is the A operand straight from HBM (lane l: token l%16), Q the B operand.
-//   online softmax per head on S^T: lane l holds tokens 4(l/16)..+3 of head l%16, which is
-//       also the A-operand layout of P in the next product.
-//   O[head][d] += P[head][token] . V[token][d]     16x16x16 MFMAs, one per 16 columns;
-//       P is split into two operand-type terms (hi + lo) so that it keeps ~16 more bits
-//       than one 16-bit rounding; V goes through a per-wave LDS tile (row padded by 16
-//       bytes so the four token groups of a read hit disjoint banks) to reach the B-operand
-//       layout (lane l: column l%16, tokens 4(l/16)..+3).
+// a 16x16 tile; unused rows carry zero queries).  Per 16-token block, with lane l in
+// row group g = l/16 and column c = l%16:
+//   S^T[m][head] = K[tok(m)][:] . Q[head][:]     16x16x32 MFMAs over the head dim, K as
+//       the A operand straight from HBM, Q the B operand.  Row m of the tile is token
+//       tok(m) = 4(m%4) + m/4 of the block: a relabelling the contraction does not see,
+//       chosen so that lane l's rows m = 4g..4g+3 are tokens g, g+4, g+8, g+12, the four
+//       V rows the same lane loads.
+//   online softmax per head on S^T (lane l: rows 4g..4g+3 of head c), which is also the
+//       A-operand layout of P in the next product.
+//   O[head][col] += P[head][m] . V[tok(m)][col]   16x16x16 MFMAs, one per tile t < D/16;
+//       tile t's column n is head-dim index E n + t (E = D/16), so lane l's B operand is
+//       element t of its four V loads (columns E c .. E c + E - 1): V reaches the matrix
+//       cores from registers.  P is split into two operand-type terms (hi + lo), keeping
+//       ~16 more bits than one 16-bit rounding.
+// At the end lane l holds columns E c .. E c + E - 1 of heads 4g..4g+3 (contiguous stores).
 // FP8 caches are widened to the query's 16-bit type (exactly) before the products; the
 // per-token scales multiply the scores and P.
+template <int N> struct Bytes;
+template <> struct Bytes<4> { using T = uint32_t; };
+template <> struct Bytes<8> { using T = uint2; };
+template <> struct Bytes<16> { using T = uint4; };
+
+template <typename W>
+__device__ __forceinline__ void words_of(const W& w, uint32_t* out);
+template <>
+__device__ __forceinline__ void words_of<uint32_t>(const uint32_t& w, uint32_t* out) { out[0] = w; }
+template <>
+__device__ __forceinline__ void words_of<uint2>(const uint2& w, uint32_t* out) { out[0] = w.x; out[1] = w.y; }
+template <>
+__device__ __forceinline__ void words_of<uint4>(const uint4& w, uint32_t* out) {
+    out[0] = w.x; out[1] = w.y; out[2] = w.z; out[3] = w.w;
+}
+
 template <typename QT, typename CT, int D, int NB>
 struct MfmaSegment {
     using M = QT;
     static constexpr int EB = Storage<CT>::bytes;
     static constexpr bool kFp8 = EB == 1;
     static constexpr int KSTEPS = D / 32;          // 16x16x32 steps over the head dimension
-    static constexpr int NT = D / 16;              // 16-column output tiles
+    static constexpr int E = D / 16;               // head-dim elements per lane per V row = tiles
     static constexpr int KLOADS = kFp8 ? KSTEPS / 2 : KSTEPS;   // 16-byte K loads per lane per block
-    static constexpr int VEPL = 16 / EB;           // V cache elements per lane per 16-byte load
-    static constexpr int TPLV = D / VEPL;          // lanes per V token row
-    static constexpr int ROWSV = kWave / TPLV;     // V token rows per wave-wide load
-    static constexpr int LPBV = kBlockSize / ROWSV;
-    static constexpr int ROWB = D * 2 + 16;        // LDS bytes per V token row (16-bit, padded)
+    static constexpr int VBYTES = E * EB;          // V bytes per lane per row: 4, 8 or 16
+    using VT = typename Bytes<VBYTES>::T;
 
     struct Buf {
-        uint4 k[KLOADS], v[LPBV];
-        float4 ks, vs;
+        uint4 k[KLOADS];
+        VT v[4];
+        float ks[kFp8 ? 4 : 1], vs[kFp8 ? 4 : 1];
     };
 
     // Head-dimension index of element i (< 8) of MFMA step s for lane group g.  Any
@@ -488,17 +507,32 @@ struct MfmaSegment {
                      Mma<M>::pack_rtz(f[6], f[7])};
     }
 
+    // One lane's V row piece (E elements) as E/2 words of operand-type pairs.
+    static __device__ __forceinline__ void v_halves(const VT& v, uint32_t* h) {
+        uint32_t w[VBYTES / 4];
+        words_of<VT>(v, w);
+        if constexpr (!kFp8) {
+#pragma unroll
+            for (int k = 0; k < E / 2; ++k) h[k] = w[k];
+        } else if constexpr (E == 8) {
+            const uint4 x = widen8(w[0], w[1]);
+            h[0] = x.x; h[1] = x.y; h[2] = x.z; h[3] = x.w;
+        } else {
+            float f[4];
+            unpack4_fp8(w[0], f);
+            h[0] = Mma<M>::pack_rtz(f[0], f[1]);
+            h[1] = Mma<M>::pack_rtz(f[2], f[3]);
+        }
+    }
+
     static __device__ __forceinline__ void run(const DecodeParams& p, int lane, int b, int hg, int jb, int je,
                                                int nblk, int L, int64_t slot) {
-        __shared__ __align__(16) char lds_all[kWaves][kBlockSize * ROWB];
-        char* lds = lds_all[threadIdx.x / kWave];
         const int G = p.hpw;
         const int h0 = hg * G;
         const int hk = h0 / (p.Hq / p.Hkv);
-        const int t16 = lane & 15;
+        const int c = lane & 15;
         const int g = lane >> 4;
-        const int vrow = lane / TPLV;
-        const int vchunk = lane % TPLV;
+        const int ktok = 4 * (c & 3) + (c >> 2);   // token of A-operand row c
 
         const int32_t* table = p.block_tables + (int64_t)b * p.max_blocks;
         auto table_chunk = [&](int jbase) {
@@ -507,77 +541,70 @@ struct MfmaSegment {
         };
         int tbl = table_chunk(jb);
 
-        // Q as the B operand: lane l holds Q[head l%16][dk(s, l/16) + i]; zero past the group.
+        // Q as the B operand: lane l holds Q[head c][dk(s, g) + i]; zero past the group.
         uint4 qb[KSTEPS];
         {
-            const bool hv = t16 < G;
-            const uint16_t* qrow = (const uint16_t*)p.query + ((int64_t)b * p.Hq + h0 + (hv ? t16 : 0)) * D;
+            const bool hv = c < G;
+            const uint16_t* qrow = (const uint16_t*)p.query + ((int64_t)b * p.Hq + h0 + (hv ? c : 0)) * D;
 #pragma unroll
             for (int s = 0; s < KSTEPS; ++s) qb[s] = hv ? *(const uint4*)(qrow + dk(s, g)) : uint4{0u, 0u, 0u, 0u};
         }
 
-        f32x4_t O[NT];
+        f32x4_t O[E];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) O[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        float m = kNegInf;      // running max of head t16 (log2 units)
-        float lsum = 0.0f;      // this lane's share of the running sum of head t16
+        for (int t = 0; t < E; ++t) O[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        float m = kNegInf;      // running max of head c (log2 units)
+        float lsum = 0.0f;      // this lane's share of the running sum of head c
 
         const int64_t tok_bytes = (int64_t)p.Hkv * D * EB;
         const int64_t blk_bytes = tok_bytes * kBlockSize;
-        const uint32_t k_off = (uint32_t)(t16 * tok_bytes + (int64_t)hk * D * EB) + 16 * g;
-        const uint32_t v_off = (uint32_t)(vrow * tok_bytes + (int64_t)hk * D * EB + vchunk * 16);
-        const uint32_t v_step = (uint32_t)(ROWSV * tok_bytes);
+        const uint32_t k_off = (uint32_t)(ktok * tok_bytes + (int64_t)hk * D * EB) + 16 * g;
+        const uint32_t v_off = (uint32_t)(g * tok_bytes + (int64_t)hk * D * EB) + VBYTES * c;
+        const uint32_t v_step = (uint32_t)(4 * tok_bytes);
         const char* kbase = (const char*)p.key_cache;
         const char* vbase = (const char*)p.value_cache;
 
         auto issue = [&](int j, int jbase, Buf& bf) {
-            uint4(&kr)[KLOADS] = bf.k;
-            uint4(&vr)[LPBV] = bf.v;
-            float4& ks = bf.ks;
-            float4& vs = bf.vs;
             const int phys = __builtin_amdgcn_readlane(tbl, j - jbase);
             const bool ok = phys >= 0 && phys < p.num_blocks;
             const int64_t pb = ok ? phys : 0;
             const char* kb = kbase + pb * blk_bytes;
             const char* vb = vbase + pb * blk_bytes;
-            // K: lane l reads 16 bytes of token l%16 (16-bit: step s at byte 64 s + 16 g;
-            // FP8: steps 2c, 2c+1 at byte 64 c + 16 g).
+            // K: lane l reads 16 bytes of token ktok (16-bit: step s at byte 64 s + 16 g;
+            // FP8: steps 2i, 2i+1 at byte 64 i + 16 g).  V: rows g + 4i, E elements at E c.
 #pragma unroll
-            for (int c = 0; c < KLOADS; ++c) kr[c] = *(const uint4*)(kb + k_off + 64 * c);
+            for (int i = 0; i < KLOADS; ++i) bf.k[i] = *(const uint4*)(kb + k_off + 64 * i);
 #pragma unroll
-            for (int i = 0; i < LPBV; ++i) vr[i] = *(const uint4*)(vb + v_off + i * v_step);
+            for (int i = 0; i < 4; ++i) bf.v[i] = *(const VT*)(vb + v_off + i * v_step);
             if constexpr (kFp8) {
-                ks = *(const float4*)(p.k_scale + pb * kBlockSize + 4 * g);
-                vs = *(const float4*)(p.v_scale + pb * kBlockSize + 4 * g);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    bf.ks[r] = p.k_scale[pb * kBlockSize + 4 * r + g];
+                    bf.vs[r] = p.v_scale[pb * kBlockSize + 4 * r + g];
+                }
             }
             return ok;
         };
 
         auto consume = [&](int j, const Buf& bf) {
-            const uint4(&kr)[KLOADS] = bf.k;
-            const uint4(&vr)[LPBV] = bf.v;
-            const float4& ks = bf.ks;
-            const float4& vs = bf.vs;
-            // S^T for the block's 16 tokens x 16 head rows.
+            // S^T for the block's 16 tokens x 16 head rows; lane l's rows 4g + r are token 4r + g.
             f32x4_t S = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
             if constexpr (!kFp8) {
 #pragma unroll
-                for (int s = 0; s < KSTEPS; ++s) S = Mma<M>::k32(kr[s], qb[s], S);
+                for (int s = 0; s < KSTEPS; ++s) S = Mma<M>::k32(bf.k[s], qb[s], S);
             } else {
 #pragma unroll
-                for (int c = 0; c < KLOADS; ++c) {
-                    S = Mma<M>::k32(widen8(kr[c].x, kr[c].y), qb[2 * c], S);
-                    S = Mma<M>::k32(widen8(kr[c].z, kr[c].w), qb[2 * c + 1], S);
+                for (int i = 0; i < KLOADS; ++i) {
+                    S = Mma<M>::k32(widen8(bf.k[i].x, bf.k[i].y), qb[2 * i], S);
+                    S = Mma<M>::k32(widen8(bf.k[i].z, bf.k[i].w), qb[2 * i + 1], S);
                 }
             }
-            const float ksc[4] = {ks.x, ks.y, ks.z, ks.w};
-            const float vsc[4] = {vs.x, vs.y, vs.z, vs.w};
             float sc[4];
             bool valid[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                valid[r] = j * kBlockSize + 4 * g + r < L;
-                const float f = kFp8 ? p.scale_log2 * ksc[r] : p.scale_log2;
+                valid[r] = j * kBlockSize + 4 * r + g < L;
+                const float f = kFp8 ? p.scale_log2 * bf.ks[r] : p.scale_log2;
                 sc[r] = valid[r] ? S[r] * f : kNegInf;
             }
             float mb = __builtin_fmaxf(__builtin_fmaxf(sc[0], sc[1]), __builtin_fmaxf(sc[2], sc[3]));
@@ -593,7 +620,7 @@ struct MfmaSegment {
             for (int r = 0; r < 4; ++r) {
                 pr[r] = fast_exp2(sc[r] - ms);
                 psum += pr[r];
-                if constexpr (kFp8) pr[r] = valid[r] ? pr[r] * vsc[r] : 0.0f;
+                if constexpr (kFp8) pr[r] = valid[r] ? pr[r] * bf.vs[r] : 0.0f;
             }
             lsum = lsum * alpha + psum;
             // Rescale the output rows (heads 4g + r) when some running max moved.
@@ -602,26 +629,21 @@ struct MfmaSegment {
                 for (int r = 0; r < 4; ++r) {
                     const float ar = __shfl(alpha, 4 * g + r);
 #pragma unroll
-                    for (int t = 0; t < NT; ++t) O[t][r] *= ar;
+                    for (int t = 0; t < E; ++t) O[t][r] *= ar;
                 }
             }
 
-            // V rows of the block into this wave's LDS tile as operand-type values; rows past
-            // the context are written as zeros (P is zero there, and 0 * NaN would not be).
+            // V rows g + 4i as operand-type pairs; rows past the context select zeros (P is
+            // zero there, and 0 * NaN would not be).
+            uint32_t vh[4][E / 2];
 #pragma unroll
-            for (int i = 0; i < LPBV; ++i) {
-                const int row = i * ROWSV + vrow;
-                const bool vv = j * kBlockSize + row < L;
-                const uint4 w = vv ? vr[i] : uint4{0u, 0u, 0u, 0u};
-                if constexpr (!kFp8) {
-                    *(uint4*)(lds + row * ROWB + vchunk * 16) = w;
-                } else {
-                    *(uint4*)(lds + row * ROWB + vchunk * 32) = widen8(w.x, w.y);
-                    *(uint4*)(lds + row * ROWB + vchunk * 32 + 16) = widen8(w.z, w.w);
-                }
+            for (int i = 0; i < 4; ++i) {
+                v_halves(bf.v[i], vh[i]);
+#pragma unroll
+                for (int k = 0; k < E / 2; ++k) vh[i][k] = valid[i] ? vh[i][k] : 0u;
             }
 
-            // P = hi + lo in the operand type (A operand: head l%16, tokens 4g..4g+3).
+            // P = hi + lo in the operand type (A operand: head c, rows 4g..4g+3).
             const uint32_t h01 = Mma<M>::pack_rtz(pr[0], pr[1]);
             const uint32_t h23 = Mma<M>::pack_rtz(pr[2], pr[3]);
             const float2_t f01 = unpack2(M{}, h01);
@@ -629,15 +651,17 @@ struct MfmaSegment {
             const uint2 a_hi = uint2{h01, h23};
             const uint2 a_lo = uint2{Mma<M>::pack_rtz(pr[0] - f01.x, pr[1] - f01.y),
                                      Mma<M>::pack_rtz(pr[2] - f23.x, pr[3] - f23.y)};
-            const uint16_t* vt = (const uint16_t*)lds;
 #pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const int col = 16 * t + t16;
-                const uint32_t e0 = vt[((4 * g + 0) * ROWB) / 2 + col];
-                const uint32_t e1 = vt[((4 * g + 1) * ROWB) / 2 + col];
-                const uint32_t e2 = vt[((4 * g + 2) * ROWB) / 2 + col];
-                const uint32_t e3 = vt[((4 * g + 3) * ROWB) / 2 + col];
-                const uint2 bt = uint2{e0 | (e1 << 16), e2 | (e3 << 16)};
+            for (int t = 0; t < E; ++t) {
+                const int k = t >> 1;
+                uint2 bt;
+                if (t & 1) {
+                    bt.x = (vh[0][k] >> 16) | (vh[1][k] & 0xFFFF0000u);
+                    bt.y = (vh[2][k] >> 16) | (vh[3][k] & 0xFFFF0000u);
+                } else {
+                    bt.x = (vh[0][k] & 0xFFFFu) | (vh[1][k] << 16);
+                    bt.y = (vh[2][k] & 0xFFFFu) | (vh[3][k] << 16);
+                }
                 O[t] = Mma<M>::k16(a_hi, bt, O[t]);
                 O[t] = Mma<M>::k16(a_lo, bt, O[t]);
             }
@@ -656,18 +680,27 @@ struct MfmaSegment {
             if (head >= G) continue;
             if (whole) {
                 const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
-                uint16_t* orow = (uint16_t*)p.out + ((int64_t)b * p.Hq + h0 + head) * D;
+                uint32_t packed[E / 2];
 #pragma unroll
-                for (int t = 0; t < NT; ++t) orow[16 * t + t16] = to_bits(QT{}, O[t][r] * inv);
+                for (int k = 0; k < E / 2; ++k)
+                    packed[k] = (uint32_t)to_bits(QT{}, O[2 * k][r] * inv) |
+                                ((uint32_t)to_bits(QT{}, O[2 * k + 1][r] * inv) << 16);
+                uint16_t* orow = (uint16_t*)p.out + ((int64_t)b * p.Hq + h0 + head) * D + E * c;
+                if constexpr (E == 8) {
+                    *(uint4*)orow = uint4{packed[0], packed[1], packed[2], packed[3]};
+                } else {
+                    *(uint2*)orow = uint2{packed[0], packed[1]};
+                }
             } else {
-                float* arow = p.ws_acc + (slot * G + head) * D;
+                float4* arow = (float4*)(p.ws_acc + (slot * G + head) * D + E * c);
 #pragma unroll
-                for (int t = 0; t < NT; ++t) arow[16 * t + t16] = O[t][r];
+                for (int q = 0; q < E / 4; ++q)
+                    arow[q] = float4{O[4 * q][r], O[4 * q + 1][r], O[4 * q + 2][r], O[4 * q + 3][r]};
             }
         }
-        if (!whole && g == 0 && t16 < G) {
-            p.ws_ml[(slot * G + t16) * 2] = m;
-            p.ws_ml[(slot * G + t16) * 2 + 1] = ltot;
+        if (!whole && g == 0 && c < G) {
+            p.ws_ml[(slot * G + c) * 2] = m;
+            p.ws_ml[(slot * G + c) * 2 + 1] = ltot;
         }
     }
 };
