@@ -63,6 +63,34 @@ def algorithmic_bytes(w):
     return kv + q + table
 
 
+def measured_traffic(workload):
+    """HBM bytes per decode call from the committed FETCH_SIZE / WRITE_SIZE summary, or None.
+
+    profiles/decode_traffic_<workload>.txt records the counter-derived bytes (scaled by the
+    plain-copy calibration) together with a SHA-256 of the kernel sources it was taken with;
+    the figure is only reported while those sources are unchanged.
+    """
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"decode_traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path, encoding="utf-8"):
+        if ":" in line and line.split(":", 1)[0] in ("traffic_bytes_per_call", "kernel_sources",
+                                                      "kernel_sources_sha256"):
+            k, v = line.split(":", 1)
+            fields[k] = v.strip()
+    if len(fields) != 3:
+        return None
+    h = hashlib.sha256()
+    for src in fields["kernel_sources"].split():
+        try:
+            h.update(open(os.path.join(ROOT, src), "rb").read())
+        except OSError:
+            return None
+    return int(fields["traffic_bytes_per_call"]) if h.hexdigest() == fields["kernel_sources_sha256"] else None
+
+
 def time_workload(name, steps, warmup, replicas, snapshot=False, partition_size=None, use_graphs=False):
     import torch
     import paged_kv_cache_187_amd as pa
@@ -277,7 +305,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": s["frac_of_peak"],
-            "traffic": None,
+            "traffic": measured_traffic(args.workload),
             "bytes_per_launch": s["algorithmic_bytes"],
             "launch_us_mean": s["decode_us_mean"],
             "launch_us_p10_p50_p90": s["decode_us_p10_p50_p90"],
