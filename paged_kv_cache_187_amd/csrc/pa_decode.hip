@@ -498,13 +498,10 @@ struct MfmaSegment {
         return kFp8 ? 64 * (s / 2) + 16 * g + 8 * (s % 2) : 32 * s + 8 * g;
     }
 
-    // Eight FP8 codes (two words) -> eight operand-type values (exact).
+    // Eight FP8 codes (two words) -> eight operand-type values (exact), two per instruction.
     static __device__ __forceinline__ uint4 widen8(uint32_t w0, uint32_t w1) {
-        float f[8];
-        unpack4_fp8(w0, f);
-        unpack4_fp8(w1, f + 4);
-        return uint4{Mma<M>::pack_rtz(f[0], f[1]), Mma<M>::pack_rtz(f[2], f[3]), Mma<M>::pack_rtz(f[4], f[5]),
-                     Mma<M>::pack_rtz(f[6], f[7])};
+        return uint4{Mma<M>::template widen2<false>(w0), Mma<M>::template widen2<true>(w0),
+                     Mma<M>::template widen2<false>(w1), Mma<M>::template widen2<true>(w1)};
     }
 
     // One lane's V row piece (E elements) as E/2 words of operand-type pairs.
@@ -514,14 +511,12 @@ struct MfmaSegment {
         if constexpr (!kFp8) {
 #pragma unroll
             for (int k = 0; k < E / 2; ++k) h[k] = w[k];
-        } else if constexpr (E == 8) {
-            const uint4 x = widen8(w[0], w[1]);
-            h[0] = x.x; h[1] = x.y; h[2] = x.z; h[3] = x.w;
         } else {
-            float f[4];
-            unpack4_fp8(w[0], f);
-            h[0] = Mma<M>::pack_rtz(f[0], f[1]);
-            h[1] = Mma<M>::pack_rtz(f[2], f[3]);
+#pragma unroll
+            for (int k = 0; k < E / 2; k += 2) {
+                h[k] = Mma<M>::template widen2<false>(w[k / 2]);
+                h[k + 1] = Mma<M>::template widen2<true>(w[k / 2]);
+            }
         }
     }
 

@@ -145,6 +145,12 @@ struct Mma<BF16> {
     static __device__ __forceinline__ uint32_t pack_rtz(float lo, float hi) {
         return (__float_as_uint(hi) & 0xFFFF0000u) | (__float_as_uint(lo) >> 16);
     }
+    // E4M3 codes in bytes 2*SEL, 2*SEL+1 of w -> one packed pair (exact: every E4M3 value
+    // is a bf16 value; the scale is 1).
+    template <bool SEL>
+    static __device__ __forceinline__ uint32_t widen2(uint32_t w) {
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, SEL));
+    }
 };
 
 template <>
@@ -159,6 +165,12 @@ struct Mma<F16> {
     }
     static __device__ __forceinline__ uint32_t pack_rtz(float lo, float hi) {
         return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+    }
+    // E4M3 codes in bytes 2*SEL, 2*SEL+1 of w -> one packed pair (exact: every E4M3 value
+    // is an f16 value; the scale is 1).
+    template <bool SEL>
+    static __device__ __forceinline__ uint32_t widen2(uint32_t w) {
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, SEL));
     }
 };
 

@@ -80,11 +80,16 @@ def test_fp8_cache_sweep(qd, D, hq, hkv, part):
     _run_and_check(cfg, what=f"fp8 D={D} G={hq // hkv} part={part}")
 
 
-def test_fp8_every_code_through_single_token_contexts():
-    """L = 1: the weight is exactly 1, so out = decode(V code) * v_scale, exact in bfloat16."""
-    _say("fp8 every code, single-token contexts")
+@pytest.mark.parametrize("qd,D,hq", [("bf16", 128, 1), ("bf16", 128, 4), ("f16", 128, 4), ("bf16", 64, 4),
+                                     ("f16", 64, 8)])
+def test_fp8_every_code_through_single_token_contexts(qd, D, hq):
+    """L = 1: the weight is exactly 1, so out = decode(V code) * v_scale, exact in the query type.
+
+    hq query heads share the one KV head: hq = 1 takes the VALU path, 4 and 8 the matrix-core path.
+    """
+    _say(f"fp8 every code, single-token contexts, q={qd} D={D} heads={hq}")
     codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
-    D, hkv = 128, 1
+    hkv = 1
     B = -(-codes.size // D)
     vc = np.zeros((B, 16, hkv, D), dtype=np.uint8)
     flat = np.zeros(B * D, dtype=np.uint8)
@@ -95,16 +100,18 @@ def test_fp8_every_code_through_single_token_contexts():
     ks = np.ones((B, 16), np.float32)
     vs = np.ones((B, 16), np.float32)
     vs[:, 1:] = np.nan
-    q = torch.randn(B, 1, D, generator=torch.Generator().manual_seed(0)).to(torch.bfloat16).cuda()
+    tdt = torch.bfloat16 if qd == "bf16" else torch.float16
+    q = torch.randn(B, hq, D, generator=torch.Generator().manual_seed(0)).to(tdt).cuda()
     out = torch.empty_like(q)
     tables = torch.arange(B, dtype=torch.int32).view(B, 1).cuda()
     lens = torch.ones(B, dtype=torch.int32).cuda()
     pa.pa_decode(out, q, torch.from_numpy(kc).cuda(), torch.from_numpy(vc).cuda(), tables, lens, 0.1, 1,
                  k_scale=torch.from_numpy(ks).cuda(), v_scale=torch.from_numpy(vs).cuda())
     torch.cuda.synchronize()
-    got = out.cpu().to(torch.float64).numpy().reshape(-1)[:codes.size]
     want = oracle.decode_e4m3(codes)
-    assert np.array_equal(got, want)
+    for h in range(hq):
+        got = out[:, h].cpu().to(torch.float64).numpy().reshape(-1)[:codes.size]
+        assert np.array_equal(got, want), f"head {h}"
 
 
 def test_poison_never_reaches_the_output_and_runs_are_deterministic():
