@@ -443,21 +443,20 @@ static __device__ __forceinline__ void run(const DecodeParams& p, int lane, int 
 // Matrix-core path for head groups of 3..16 query heads sharing one KV head (rows of
 // a 16x16 tile; unused rows carry zero queries).  Per 16-token block, with lane l in
 // row group g = l/16 and column c = l%16:
-//   S^T[m][head] = K[tok(m)][:] . Q[head][:]     16x16x32 MFMAs over the head dim, K as
-//       the A operand straight from HBM, Q the B operand.  Row m of the tile is token
-//       tok(m) = 4(m%4) + m/4 of the block: a relabelling the contraction does not see,
-//       chosen so that lane l's rows m = 4g..4g+3 are tokens g, g+4, g+8, g+12, the four
-//       V rows the same lane loads.
-//   online softmax per head on S^T (lane l: rows 4g..4g+3 of head c), which is also the
+//   S^T[token][head] = K[token][:] . Q[head][:]   16x16x32 MFMAs over the head dim, K as
+//       the A operand straight from HBM (lane l: token c), Q the B operand.
+//   online softmax per head on S^T (lane l: tokens 4g..4g+3 of head c), which is also the
 //       A-operand layout of P in the next product.
-//   O[head][col] += P[head][m] . V[tok(m)][col]   16x16x16 MFMAs, one per tile t < D/16;
-//       tile t's column n is head-dim index E n + t (E = D/16), so lane l's B operand is
-//       element t of its four V loads (columns E c .. E c + E - 1): V reaches the matrix
-//       cores from registers.  P is split into two operand-type terms (hi + lo), keeping
-//       ~16 more bits than one 16-bit rounding.
+//   O[head][col] += P[head][token] . V[token][col]   16x16x16 MFMAs, one per tile t < D/16;
+//       V load i brings lane l the E = D/16 elements E c .. E c + E - 1 of token 4g + i,
+//       and tile t's column n is head-dim index E n + t, so lane l's B operand for tile t
+//       is element t of its four V loads: V reaches the matrix cores from registers.  P is
+//       split into two operand-type terms (hi + lo), keeping ~16 more bits than one 16-bit
+//       rounding.
 // At the end lane l holds columns E c .. E c + E - 1 of heads 4g..4g+3 (contiguous stores).
 // FP8 caches are widened to the query's 16-bit type (exactly) before the products; the
-// per-token scales multiply the scores and P.
+// per-token scales (four consecutive tokens per lane: one 16-byte load each for K and V)
+// multiply the scores and P.
 template <int N> struct Bytes;
 template <> struct Bytes<4> { using T = uint32_t; };
 template <> struct Bytes<8> { using T = uint2; };
@@ -488,7 +487,7 @@ struct MfmaSegment {
     struct Buf {
         uint4 k[KLOADS];
         VT v[4];
-        float ks[kFp8 ? 4 : 1], vs[kFp8 ? 4 : 1];
+        float4 ks, vs;
     };
 
     // Head-dimension index of element i (< 8) of MFMA step s for lane group g.  Any
@@ -527,7 +526,6 @@ struct MfmaSegment {
         const int hk = h0 / (p.Hq / p.Hkv);
         const int c = lane & 15;
         const int g = lane >> 4;
-        const int ktok = 4 * (c & 3) + (c >> 2);   // token of A-operand row c
 
         const int32_t* table = p.block_tables + (int64_t)b * p.max_blocks;
         auto table_chunk = [&](int jbase) {
@@ -553,9 +551,9 @@ struct MfmaSegment {
 
         const int64_t tok_bytes = (int64_t)p.Hkv * D * EB;
         const int64_t blk_bytes = tok_bytes * kBlockSize;
-        const uint32_t k_off = (uint32_t)(ktok * tok_bytes + (int64_t)hk * D * EB) + 16 * g;
-        const uint32_t v_off = (uint32_t)(g * tok_bytes + (int64_t)hk * D * EB) + VBYTES * c;
-        const uint32_t v_step = (uint32_t)(4 * tok_bytes);
+        const uint32_t k_off = (uint32_t)(c * tok_bytes + (int64_t)hk * D * EB) + 16 * g;
+        const uint32_t v_off = (uint32_t)(4 * g * tok_bytes + (int64_t)hk * D * EB) + VBYTES * c;
+        const uint32_t v_step = (uint32_t)tok_bytes;
         const char* kbase = (const char*)p.key_cache;
         const char* vbase = (const char*)p.value_cache;
 
@@ -565,24 +563,21 @@ struct MfmaSegment {
             const int64_t pb = ok ? phys : 0;
             const char* kb = kbase + pb * blk_bytes;
             const char* vb = vbase + pb * blk_bytes;
-            // K: lane l reads 16 bytes of token ktok (16-bit: step s at byte 64 s + 16 g;
-            // FP8: steps 2i, 2i+1 at byte 64 i + 16 g).  V: rows g + 4i, E elements at E c.
+            // K: lane l reads 16 bytes of token c (16-bit: step s at byte 64 s + 16 g;
+            // FP8: steps 2i, 2i+1 at byte 64 i + 16 g).  V: rows 4g + i, E elements at E c.
 #pragma unroll
             for (int i = 0; i < KLOADS; ++i) bf.k[i] = *(const uint4*)(kb + k_off + 64 * i);
 #pragma unroll
             for (int i = 0; i < 4; ++i) bf.v[i] = *(const VT*)(vb + v_off + i * v_step);
             if constexpr (kFp8) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    bf.ks[r] = p.k_scale[pb * kBlockSize + 4 * r + g];
-                    bf.vs[r] = p.v_scale[pb * kBlockSize + 4 * r + g];
-                }
+                bf.ks = *(const float4*)(p.k_scale + pb * kBlockSize + 4 * g);
+                bf.vs = *(const float4*)(p.v_scale + pb * kBlockSize + 4 * g);
             }
             return ok;
         };
 
         auto consume = [&](int j, const Buf& bf) {
-            // S^T for the block's 16 tokens x 16 head rows; lane l's rows 4g + r are token 4r + g.
+            // S^T for the block's 16 tokens x 16 head rows (lane l: tokens 4g + r of head c).
             f32x4_t S = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
             if constexpr (!kFp8) {
 #pragma unroll
@@ -594,12 +589,14 @@ struct MfmaSegment {
                     S = Mma<M>::k32(widen8(bf.k[i].z, bf.k[i].w), qb[2 * i + 1], S);
                 }
             }
+            const float ksc[4] = {bf.ks.x, bf.ks.y, bf.ks.z, bf.ks.w};
+            const float vsc[4] = {bf.vs.x, bf.vs.y, bf.vs.z, bf.vs.w};
             float sc[4];
             bool valid[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                valid[r] = j * kBlockSize + 4 * r + g < L;
-                const float f = kFp8 ? p.scale_log2 * bf.ks[r] : p.scale_log2;
+                valid[r] = j * kBlockSize + 4 * g + r < L;
+                const float f = kFp8 ? p.scale_log2 * ksc[r] : p.scale_log2;
                 sc[r] = valid[r] ? S[r] * f : kNegInf;
             }
             float mb = __builtin_fmaxf(__builtin_fmaxf(sc[0], sc[1]), __builtin_fmaxf(sc[2], sc[3]));
@@ -615,7 +612,7 @@ struct MfmaSegment {
             for (int r = 0; r < 4; ++r) {
                 pr[r] = fast_exp2(sc[r] - ms);
                 psum += pr[r];
-                if constexpr (kFp8) pr[r] = valid[r] ? pr[r] * bf.vs[r] : 0.0f;
+                if constexpr (kFp8) pr[r] = valid[r] ? pr[r] * vsc[r] : 0.0f;
             }
             lsum = lsum * alpha + psum;
             // Rescale the output rows (heads 4g + r) when some running max moved.
@@ -628,7 +625,7 @@ struct MfmaSegment {
                 }
             }
 
-            // V rows g + 4i as operand-type pairs; rows past the context select zeros (P is
+            // V rows 4g + i as operand-type pairs; rows past the context select zeros (P is
             // zero there, and 0 * NaN would not be).
             uint32_t vh[4][E / 2];
 #pragma unroll
