@@ -175,6 +175,45 @@ def time_workload(name, steps, warmup, replicas, snapshot=False, partition_size=
     }
 
 
+def time_copy_blocks(steps, warmup, pairs, num_blocks=4096, replicas=2):
+    """pa_copy_blocks on llama7b-shaped blocks (32 KV heads x 128 x f16: 128 KiB per pool per block).
+
+    `pairs` random (src, dst) pairs with distinct destinations that are never sources; bytes moved
+    per call = pairs x 2 pools x 128 KiB, read once and written once.  Pools of `num_blocks` blocks
+    (1 GiB for both pools at 4096) alternate between calls so the data comes from HBM.
+    """
+    import numpy as np
+    import torch
+    import paged_kv_cache_187_amd as pa
+
+    hkv, d = 32, 128
+    block_bytes = 16 * hkv * d * 2
+    pools = []
+    for r in range(replicas):
+        pools.append((torch.empty(num_blocks, 16, hkv, d, dtype=torch.float16, device="cuda").normal_(),
+                      torch.empty(num_blocks, 16, hkv, d, dtype=torch.float16, device="cuda").normal_()))
+    ids = np.random.default_rng(5).permutation(num_blocks)
+    mapping = torch.from_numpy(np.stack([ids[:pairs], ids[pairs:2 * pairs]], 1).astype(np.int64)).cuda()
+    for i in range(warmup):
+        pa.pa_copy_blocks(*pools[i % replicas], mapping)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i, (a, b) in enumerate(ev):
+        a.record(stream)
+        pa.pa_copy_blocks(*pools[i % replicas], mapping)
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+    mean = sum(us) / len(us)
+    moved = pairs * 2 * block_bytes * 2
+    return {"pairs": pairs, "block_bytes_per_pool": block_bytes, "bytes_moved": moved,
+            "us_mean": round(mean, 2), "us_p10_p50_p90": [round(us[len(us) // 10], 2), round(us[len(us) // 2], 2),
+                                                          round(us[(9 * len(us)) // 10], 2)],
+            "effective_GBs": round(moved / (mean * 1e-6) / 1e9, 1),
+            "frac_of_peak": round(moved / (mean * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def cpu_baseline(w, host, min_seconds):
     """The float64 oracle on the host, on the same workload (pre-step state), single-threaded."""
     import numpy as np
@@ -238,6 +277,7 @@ def main():
                     "and decode instead of launching from Python (slower on ROCm 7 for this two-launch step)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (5 times), to scale rocprofv3 FETCH_SIZE/WRITE_SIZE")
+    ap.add_argument("--no-copy", action="store_true", help="skip the pa_copy_blocks measurement")
     ap.add_argument("--partition-size", type=int, default=None,
                     help="override the workload's partition length (tokens; 0 = library's choice)")
     args = ap.parse_args()
@@ -275,6 +315,11 @@ def main():
                           use_graphs=args.graphs)
         also[name] = summarize(name, r)
         del r
+        torch.cuda.empty_cache()
+
+    if not args.no_copy:
+        also["copy_blocks"] = {"bandwidth": time_copy_blocks(args.steps, args.warmup, 1024),
+                               "copy_on_write_64_pairs": time_copy_blocks(args.steps, args.warmup, 64)}
         torch.cuda.empty_cache()
 
     result = {

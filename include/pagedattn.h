@@ -1,7 +1,7 @@
 /*
  * pagedattn.h - C ABI of the gfx950 (MI355X) paged decode attention library.
  *
- * Two operations, both from the pages' description of PagedAttention:
+ * Three operations, all from the pages' description of PagedAttention:
  *
  *  - pa_append_kv: write each new token's K and V rows into the slot of the
  *    KV cache that the block manager gave it ("大模型推理引擎优化：KV Cache 与连续批处理",
@@ -15,6 +15,10 @@
  *    the sequence's page table; the kernel turns logical token indices into
  *    physical addresses, so the result is plain softmax attention over the
  *    tokens in logical order ("LLM推理引擎深度实战：…", §2.2 and §2.3).
+ *
+ *  - pa_copy_blocks: copy whole physical blocks, the copy-on-write step the
+ *    block manager takes before a sequence writes into a block that other
+ *    sequences share ("大模型推理引擎优化：…", §4.2; "LLM推理引擎深度实战：…", §2.2).
  *
  * Layouts (all row-major, contiguous, little-endian):
  *   query        [num_seqs, num_heads, head_dim]                 q_dtype
@@ -108,6 +112,26 @@ pa_status pa_append_kv(const void *key, const void *value,
                        int64_t num_blocks,
                        int32_t src_dtype, int32_t cache_dtype,
                        void *stream);
+
+/*
+ * pa_copy_blocks - for every pair i < num_pairs with (src, dst) =
+ * (block_mapping[2 i], block_mapping[2 i + 1]): copy physical block src of
+ * key_cache to block dst, likewise for value_cache, and for an FP8 cache the
+ * block's 16 scales of k_scale and of v_scale, bit for bit.
+ *
+ * block_mapping: [num_pairs, 2] int64, device.  Pairs with src or dst outside
+ * [0, num_blocks), or src == dst, are skipped.  The destinations of one call
+ * must be distinct and must not be the source of another pair in the same
+ * call (otherwise which bytes a block ends up with is undefined).  cache_dtype
+ * F16, BF16 or FP8_E4M3 (k_scale / v_scale required for FP8, ignored
+ * otherwise).  head_dim 64 or 128.  Caches 16-byte aligned, block_mapping
+ * 8-byte aligned, scales 4-byte aligned.
+ */
+pa_status pa_copy_blocks(void *key_cache, void *value_cache,
+                         float *k_scale, float *v_scale,
+                         const int64_t *block_mapping, int64_t num_pairs,
+                         int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                         int32_t cache_dtype, void *stream);
 
 /*
  * pa_decode_partition_size - how pa_decode splits the work for these

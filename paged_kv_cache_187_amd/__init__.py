@@ -1,4 +1,4 @@
-"""gfx950 (MI355X) paged decode attention and slot-mapped KV append.
+"""gfx950 (MI355X) paged decode attention, slot-mapped KV append and copy-on-write block copy.
 
 The work runs in hand-written HIP kernels behind the C ABI declared in
 ``include/pagedattn.h`` (``libpagedattn.so``, built in-tree by
@@ -16,5 +16,6 @@ from .binding import (  # noqa: F401
     decode_workspace_bytes,
     load_library,
     pa_append_kv,
+    pa_copy_blocks,
     pa_decode,
 )

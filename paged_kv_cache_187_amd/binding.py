@@ -44,6 +44,8 @@ def load_library(path=LIB_PATH):
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     lib.pa_append_kv.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i64, i32, i32, vp]
     lib.pa_append_kv.restype = i32
+    lib.pa_copy_blocks.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i64, i32, vp]
+    lib.pa_copy_blocks.restype = i32
     lib.pa_decode_partition_size.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.pa_decode_partition_size.restype = i32
     lib.pa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
@@ -101,6 +103,23 @@ def pa_append_kv(key, value, key_cache, value_cache, slot_mapping, k_scale=None,
     _check(load_library().pa_append_kv(
         _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache), _ptr(k_scale), _ptr(v_scale),
         _ptr(slot_mapping), T, hkv, d, key_cache.shape[0], _DTYPE[key.dtype], cdt, _stream(stream)))
+
+
+def pa_copy_blocks(key_cache, value_cache, block_mapping, k_scale=None, v_scale=None, stream=None):
+    """Copy whole blocks src -> dst of both caches (and FP8 scales) for block_mapping [n, 2] int64 pairs."""
+    _on_gpu(key_cache, value_cache, block_mapping, k_scale, v_scale)
+    nb, bs, hkv, d = key_cache.shape
+    if bs != BLOCK_SIZE or value_cache.shape != key_cache.shape or block_mapping.dtype != torch.int64 or \
+            block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
+        raise ValueError("inconsistent shapes for pa_copy_blocks")
+    cdt = _DTYPE[key_cache.dtype]
+    if cdt == PA_FP8_E4M3:
+        for s in (k_scale, v_scale):
+            if s is None or s.dtype != torch.float32 or s.shape != key_cache.shape[:2]:
+                raise ValueError("FP8 cache needs float32 k_scale / v_scale shaped [num_blocks, 16]")
+    _check(load_library().pa_copy_blocks(
+        _ptr(key_cache), _ptr(value_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_mapping),
+        block_mapping.shape[0], hkv, d, nb, cdt, _stream(stream)))
 
 
 def decode_partition_size(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, partition_size=0):

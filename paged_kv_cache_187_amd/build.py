@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB_NAME = "libpagedattn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["pa_append.hip", "pa_decode.hip", "pa_api.cpp"]
+SOURCES = ["pa_append.hip", "pa_copy.hip", "pa_decode.hip", "pa_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 COMMON = [

@@ -117,6 +117,26 @@ pa_status pa_append_kv(const void* key, const void* value, void* key_cache, void
                                           num_tokens, row_elems, num_slots, src_dtype, s));
 }
 
+pa_status pa_copy_blocks(void* key_cache, void* value_cache, float* k_scale, float* v_scale,
+                         const int64_t* block_mapping, int64_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                         int64_t num_blocks, int32_t cache_dtype, void* stream) {
+    if (num_pairs < 0 || num_pairs > ((int64_t)1 << 31) - 1 || num_kv_heads <= 0 || num_kv_heads > 4096 ||
+        num_blocks <= 0)
+        return PA_ERR_SHAPE;
+    if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+    const bool fp8 = cache_dtype == PA_FP8_E4M3;
+    if (!fp8 && !is16(cache_dtype)) return PA_ERR_DTYPE;
+    if (num_pairs == 0) return PA_OK;
+    if (!key_cache || !value_cache || !block_mapping) return PA_ERR_NULL;
+    if (fp8 && (!k_scale || !v_scale)) return PA_ERR_NULL;
+    if (!aligned(key_cache, 16) || !aligned(value_cache, 16) || !aligned(block_mapping, 8) ||
+        (fp8 && (!aligned(k_scale, 4) || !aligned(v_scale, 4))))
+        return PA_ERR_ALIGN;
+    const int64_t block_bytes = (int64_t)PA_BLOCK_SIZE * num_kv_heads * head_dim * (fp8 ? 1 : 2);
+    return from_hip(pa::launch_copy_blocks(key_cache, value_cache, fp8 ? k_scale : nullptr, fp8 ? v_scale : nullptr,
+                                           block_mapping, num_pairs, block_bytes, num_blocks, (hipStream_t)stream));
+}
+
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                                  int32_t max_context_len, int32_t partition_size) {
     const Plan pl = make_plan(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, partition_size);

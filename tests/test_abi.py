@@ -35,7 +35,7 @@ def lib():
 
 
 def test_header_declares_the_boundary():
-    assert _declared() == ["pa_append_kv", "pa_decode", "pa_decode_partition_size",
+    assert _declared() == ["pa_append_kv", "pa_copy_blocks", "pa_decode", "pa_decode_partition_size",
                            "pa_decode_workspace_bytes", "pa_status_string"]
 
 
@@ -123,6 +123,27 @@ def test_append_host_checks(lib):
     assert _append(lib, sd=FP8, cd=FP8) == DTYPE
     assert _append(lib, kc=FAKE + 8) == ALIGN
     assert _append(lib, T=0) == OK
+
+
+def _copy(lib, **kw):
+    a = dict(kc=FAKE, vc=FAKE, ks=None, vs=None, m=FAKE, n=4, Hkv=2, D=64, nb=8, cd=F16)
+    a.update(kw)
+    return lib.pa_copy_blocks(a["kc"], a["vc"], a["ks"], a["vs"], a["m"], a["n"], a["Hkv"], a["D"], a["nb"],
+                              a["cd"], None)
+
+
+def test_copy_blocks_host_checks(lib):
+    assert _copy(lib, kc=None) == NULL
+    assert _copy(lib, m=None) == NULL
+    assert _copy(lib, cd=FP8) == NULL                       # FP8 cache without scales
+    assert _copy(lib, n=-1) == SHAPE
+    assert _copy(lib, nb=0) == SHAPE
+    assert _copy(lib, Hkv=0) == SHAPE
+    assert _copy(lib, D=96) == UNSUP
+    assert _copy(lib, cd=3) == DTYPE
+    assert _copy(lib, kc=FAKE + 8) == ALIGN
+    assert _copy(lib, m=FAKE + 4) == ALIGN
+    assert _copy(lib, n=0) == OK                            # nothing to do, nothing launched
 
 
 def test_binding_rejects_host_tensors():
