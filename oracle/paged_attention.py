@@ -22,6 +22,12 @@ query head h:
 
 The gather into contiguous K/V is done first, then the attention, as the
 plain definition reads; numpy matrix products are the only library steps.
+
+Sliding window ("LLM推理引擎深度实战：…", §9.2 names sliding-window attention, as in
+Mistral, among the long-context methods without defining it; the reading taken
+is the usual one): with a window of W > 0 tokens the query of a sequence of
+length L attends only to its last W tokens, t = max(0, L - W) .. L - 1 (itself
+included).  W = 0 means no window.
 """
 
 import numpy as np
@@ -72,15 +78,20 @@ def gather_kv(cache_bits, block_table, length, dtype, scales=None):
     return out
 
 
+def window_start(length, window):
+    """First token a query attends to: max(0, L - W) with a window of W > 0 tokens, else 0."""
+    return max(0, length - window) if window > 0 else 0
+
+
 def paged_decode(query, key_cache, value_cache, block_tables, context_lens, scale,
-                 q_dtype, cache_dtype, k_scale=None, v_scale=None):
+                 q_dtype, cache_dtype, k_scale=None, v_scale=None, window=0):
     """Paged decode attention for a whole batch.
 
     query: [B, Hq, D] bit patterns (uint16) of ``q_dtype``; caches:
     [num_blocks, 16, Hkv, D] bit patterns of ``cache_dtype`` ("f16", "bf16",
     or "fp8_e4m3" with float32 k_scale / v_scale [num_blocks, 16]);
-    block_tables: int [B, max_blocks]; context_lens: int [B].
-    Returns float64 [B, Hq, D].
+    block_tables: int [B, max_blocks]; context_lens: int [B]; window: sliding
+    window in tokens (0 = none).  Returns float64 [B, Hq, D].
     """
     q = decode_bits(query, q_dtype)
     B, Hq, D = q.shape
@@ -89,22 +100,24 @@ def paged_decode(query, key_cache, value_cache, block_tables, context_lens, scal
     out = np.zeros((B, Hq, D), dtype=np.float64)
     for b in range(B):
         L = int(context_lens[b])
-        K = gather_kv(key_cache, block_tables[b], L, cache_dtype, k_scale)
-        V = gather_kv(value_cache, block_tables[b], L, cache_dtype, v_scale)
+        lo = window_start(L, window)
+        K = gather_kv(key_cache, block_tables[b], L, cache_dtype, k_scale)[lo:]
+        V = gather_kv(value_cache, block_tables[b], L, cache_dtype, v_scale)[lo:]
         for h in range(Hq):
             out[b, h] = attend(q[b, h], K[:, h // g, :], V[:, h // g, :], scale)
     return out
 
 
 def paged_decode_one(q_vec, key_cache, value_cache, block_table, length, kv_head, scale,
-                     cache_dtype, k_scale=None, v_scale=None):
+                     cache_dtype, k_scale=None, v_scale=None, window=0):
     """One (sequence, head) of ``paged_decode``, for sampled checks of large runs.
 
     q_vec: float64 [D] (already decoded); caches are bit-pattern arrays that
     need only hold the blocks ``block_table`` names.
     """
-    K = gather_kv(key_cache, block_table, length, cache_dtype, k_scale)
-    V = gather_kv(value_cache, block_table, length, cache_dtype, v_scale)
+    lo = window_start(length, window)
+    K = gather_kv(key_cache, block_table, length, cache_dtype, k_scale)[lo:]
+    V = gather_kv(value_cache, block_table, length, cache_dtype, v_scale)[lo:]
     return attend(np.asarray(q_vec, dtype=np.float64), K[:, kv_head, :], V[:, kv_head, :], scale)
 
 

@@ -228,3 +228,53 @@ def test_synth_tiny_workload_through_oracle_is_finite():
     # sequence 0 has one token, the one appended this step: its output is that token's V row
     vd = oracle.decode_f16(bits_np(w.value_new))
     assert np.array_equal(out[0], vd[0])
+
+
+@pytest.mark.parametrize("window", [0, 37, 38, 1000])
+def test_window_covering_the_context_changes_nothing(window):
+    q, kc, vc, tables, lens = _random_case(31)
+    full = oracle.paged_decode(q, kc, vc, tables, lens, 0.25, "f16", "f16")
+    win = oracle.paged_decode(q, kc, vc, tables, lens, 0.25, "f16", "f16", window=window)
+    assert np.array_equal(full, win)
+
+
+def test_window_of_one_returns_the_last_v_row():
+    q, kc, vc, tables, lens = _random_case(32)
+    out = oracle.paged_decode(q, kc, vc, tables, lens, 0.25, "f16", "f16", window=1)
+    for b, L in enumerate(lens):
+        last = oracle.decode_bits(vc, "f16")[tables[b, (L - 1) // BS], (L - 1) % BS]
+        for h in range(q.shape[1]):
+            assert np.array_equal(out[b, h], last[h // 2])
+
+
+@pytest.mark.parametrize("window", [2, 5, 16, 17, 20])
+def test_window_equals_dense_attention_over_the_last_tokens(window):
+    """Python loops over the last W tokens of each sequence, written out directly."""
+    q, kc, vc, tables, lens = _random_case(33, lens=(5, 16, 37))
+    out = oracle.paged_decode(q, kc, vc, tables, lens, 0.3, "f16", "f16", window=window)
+    qd = oracle.decode_bits(q, "f16")
+    kd, vd = oracle.decode_bits(kc, "f16"), oracle.decode_bits(vc, "f16")
+    for b, L in enumerate(lens):
+        toks = list(range(max(0, L - window), L))
+        for h in range(qd.shape[1]):
+            hk = h // 2
+            s = [0.3 * sum(qd[b, h, d] * kd[tables[b, t // BS], t % BS, hk, d] for d in range(qd.shape[2]))
+                 for t in toks]
+            mx = max(s)
+            e = [math.exp(x - mx) for x in s]
+            want = [sum(e[i] * vd[tables[b, t // BS], t % BS, hk, d] for i, t in enumerate(toks)) / sum(e)
+                    for d in range(qd.shape[2])]
+            assert np.allclose(out[b, h], want, rtol=1e-12, atol=1e-12)
+
+
+def test_tokens_before_the_window_never_reach_the_output():
+    q, kc, vc, tables, lens = _random_case(34, lens=(40, 33, 50))
+    window = 9
+    clean = oracle.paged_decode(q, kc, vc, tables, lens, 0.25, "f16", "f16", window=window)
+    kp, vp = kc.copy(), vc.copy()
+    for b, L in enumerate(lens):
+        for t in range(0, L - window):
+            kp[tables[b, t // BS], t % BS] = 0x7E00
+            vp[tables[b, t // BS], t % BS] = 0x7E00
+    poisoned = oracle.paged_decode(q, kp, vp, tables, lens, 0.25, "f16", "f16", window=window)
+    assert np.array_equal(clean, poisoned) and np.isfinite(poisoned).all()
