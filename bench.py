@@ -43,12 +43,22 @@ WORKLOAD_TEXT = {
 }
 
 
-def algorithmic_bytes(w):
-    """Bytes the method must read per decode: KV rows + scales, Q, page-table entries, lengths."""
+def algorithmic_bytes(w, window=0):
+    """Bytes the method must read per decode: KV rows + scales, Q, page-table entries, lengths.
+
+    With a sliding window only the last `window` tokens of each sequence (and the table entries
+    of their blocks) count.
+    """
     import numpy as np
     cfg = w.cfg
     eb = 1 if cfg.cache_dtype == "fp8_e4m3" else 2
     lens = w.lens_np.astype(np.int64)
+    if window > 0:
+        first = np.maximum(lens - window, 0)
+        kv_tokens = int(np.sum(lens - first))
+        blocks = int(np.sum((lens + 15) // 16 - first // 16))
+        return (kv_tokens * cfg.num_kv_heads * cfg.head_dim * 2 * eb + (kv_tokens * 8 if eb == 1 else 0)
+                + cfg.num_seqs * cfg.num_heads * cfg.head_dim * 2 + blocks * 4 + cfg.num_seqs * 4)
     if cfg.beams > 1:
         # unique bytes: shared prefix blocks counted once
         prompts = cfg.num_seqs // cfg.beams
@@ -91,7 +101,7 @@ def measured_traffic(workload):
     return int(fields["traffic_bytes_per_call"]) if h.hexdigest() == fields["kernel_sources_sha256"] else None
 
 
-def time_workload(name, steps, warmup, replicas, snapshot=False, partition_size=None, use_graphs=False):
+def time_workload(name, steps, warmup, replicas, snapshot=False, partition_size=None, use_graphs=False, window=0):
     import torch
     import paged_kv_cache_187_amd as pa
     import synth
@@ -121,8 +131,12 @@ def time_workload(name, steps, warmup, replicas, snapshot=False, partition_size=
         pa.pa_append_kv(w.key_new, w.value_new, kcs[r], vcs[r], w.slot_mapping, kss[r], vss[r])
 
     def decode(r):
-        pa.pa_decode(out, w.query, kcs[r], vcs[r], w.block_tables, w.context_lens, cfg.scale, max_len,
-                     partition_size=part, k_scale=kss[r], v_scale=vss[r], workspace=ws)
+        if window > 0:
+            pa.pa_decode_sliding(out, w.query, kcs[r], vcs[r], w.block_tables, w.context_lens, cfg.scale, max_len,
+                                 window, partition_size=part, k_scale=kss[r], v_scale=vss[r], workspace=ws)
+        else:
+            pa.pa_decode(out, w.query, kcs[r], vcs[r], w.block_tables, w.context_lens, cfg.scale, max_len,
+                         partition_size=part, k_scale=kss[r], v_scale=vss[r], workspace=ws)
 
     for i in range(warmup):
         append(i % replicas)
@@ -171,7 +185,7 @@ def time_workload(name, steps, warmup, replicas, snapshot=False, partition_size=
         "decode_ms_p90": dec_ms[min(n - 1, (9 * n) // 10)],
         "partition_size": pa.decode_partition_size(cfg.num_seqs, cfg.num_heads, cfg.num_kv_heads, cfg.head_dim,
                                                    max_len, part),
-        "bytes": algorithmic_bytes(w),
+        "bytes": algorithmic_bytes(w, window),
     }
 
 
@@ -278,6 +292,8 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (5 times), to scale rocprofv3 FETCH_SIZE/WRITE_SIZE")
     ap.add_argument("--no-copy", action="store_true", help="skip the pa_copy_blocks measurement")
+    ap.add_argument("--window", type=int, default=512,
+                    help="sliding window (tokens) of the extra pa_decode_sliding line on the main workload; 0 = skip")
     ap.add_argument("--partition-size", type=int, default=None,
                     help="override the workload's partition length (tokens; 0 = library's choice)")
     args = ap.parse_args()
@@ -317,6 +333,13 @@ def main():
         del r
         torch.cuda.empty_cache()
 
+    if args.window > 0:
+        r = time_workload(args.workload, args.steps, args.warmup, args.replicas, partition_size=args.partition_size,
+                          use_graphs=args.graphs, window=args.window)
+        also[f"{args.workload}_window{args.window}"] = summarize(args.workload, r)
+        also[f"{args.workload}_window{args.window}"]["sliding_window"] = args.window
+        del r
+        torch.cuda.empty_cache()
     if not args.no_copy:
         also["copy_blocks"] = {"bandwidth": time_copy_blocks(args.steps, args.warmup, 1024),
                                "copy_on_write_64_pairs": time_copy_blocks(args.steps, args.warmup, 64)}

@@ -1,7 +1,7 @@
 /*
  * pagedattn.h - C ABI of the gfx950 (MI355X) paged decode attention library.
  *
- * Three operations, all from the pages' description of PagedAttention:
+ * The operations, all from the pages' description of PagedAttention:
  *
  *  - pa_append_kv: write each new token's K and V rows into the slot of the
  *    KV cache that the block manager gave it ("大模型推理引擎优化：KV Cache 与连续批处理",
@@ -14,7 +14,8 @@
  *    cached K/V, which sit in fixed 16-token physical blocks reached through
  *    the sequence's page table; the kernel turns logical token indices into
  *    physical addresses, so the result is plain softmax attention over the
- *    tokens in logical order ("LLM推理引擎深度实战：…", §2.2 and §2.3).
+ *    tokens in logical order ("LLM推理引擎深度实战：…", §2.2 and §2.3);
+ *    pa_decode_sliding restricts it to a sliding window of recent tokens.
  *
  *  - pa_copy_blocks: copy whole physical blocks, the copy-on-write step the
  *    block manager takes before a sequence writes into a block that other
@@ -201,6 +202,29 @@ pa_status pa_decode(void *out, const void *query,
                     int32_t q_dtype, int32_t cache_dtype,
                     void *workspace, size_t workspace_bytes,
                     void *stream);
+
+/*
+ * pa_decode_sliding - pa_decode with a sliding window: the query of a
+ * sequence of length L attends only to its last sliding_window tokens,
+ * t = max(0, L - sliding_window) .. L - 1 ("LLM推理引擎深度实战：…", §9.2 names
+ * sliding-window attention among the long-context methods).  Only the blocks
+ * holding those tokens are read; tokens before the window are excluded by
+ * selection, so whatever their slots hold never reaches out.
+ * sliding_window == 0 is pa_decode; negative values return PA_ERR_SHAPE.
+ * Every other argument, the workspace (same pa_decode_workspace_bytes) and
+ * the determinism guarantee are those of pa_decode.
+ */
+pa_status pa_decode_sliding(void *out, const void *query,
+                            const void *key_cache, const void *value_cache,
+                            const float *k_scale, const float *v_scale,
+                            const int32_t *block_tables, const int32_t *context_lens,
+                            int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int64_t num_blocks,
+                            int32_t max_blocks_per_seq, int32_t max_context_len,
+                            float scale, int32_t partition_size,
+                            int32_t q_dtype, int32_t cache_dtype,
+                            void *workspace, size_t workspace_bytes,
+                            void *stream, int32_t sliding_window);
 
 /* pa_status_string - static, human-readable name of a status code. */
 const char *pa_status_string(int32_t status);

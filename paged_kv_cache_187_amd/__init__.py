@@ -18,4 +18,5 @@ from .binding import (  # noqa: F401
     pa_append_kv,
     pa_copy_blocks,
     pa_decode,
+    pa_decode_sliding,
 )

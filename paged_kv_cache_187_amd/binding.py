@@ -53,6 +53,8 @@ def load_library(path=LIB_PATH):
     lib.pa_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i64, i32, i32,
                               ctypes.c_float, i32, i32, i32, vp, sz, vp]
     lib.pa_decode.restype = i32
+    lib.pa_decode_sliding.argtypes = lib.pa_decode.argtypes + [i32]
+    lib.pa_decode_sliding.restype = i32
     lib.pa_status_string.argtypes = [i32]
     lib.pa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -150,6 +152,19 @@ def pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, sc
     block_tables [B, max_blocks] int32, context_lens [B] int32; max_context_len is a host-side
     upper bound of context_lens.  A workspace is allocated here when none is passed.
     """
+    return _decode(None, out, query, key_cache, value_cache, block_tables, context_lens, scale, max_context_len,
+                   partition_size, k_scale, v_scale, workspace, stream)
+
+
+def pa_decode_sliding(out, query, key_cache, value_cache, block_tables, context_lens, scale, max_context_len,
+                      sliding_window, partition_size=0, k_scale=None, v_scale=None, workspace=None, stream=None):
+    """pa_decode over each sequence's last ``sliding_window`` tokens only (0 = the whole context)."""
+    return _decode(int(sliding_window), out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                   max_context_len, partition_size, k_scale, v_scale, workspace, stream)
+
+
+def _decode(window, out, query, key_cache, value_cache, block_tables, context_lens, scale, max_context_len,
+            partition_size, k_scale, v_scale, workspace, stream):
     _on_gpu(out, query, key_cache, value_cache, block_tables, context_lens, k_scale, v_scale, workspace)
     B, hq, d = query.shape
     nb, bs, hkv, dk = key_cache.shape
@@ -161,9 +176,10 @@ def pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, sc
     if workspace is None:
         workspace = alloc_workspace(query, hkv, max_context_len, partition_size)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(load_library().pa_decode(
-        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(k_scale), _ptr(v_scale),
-        _ptr(block_tables), _ptr(context_lens), B, hq, hkv, d, nb, block_tables.shape[1],
-        int(max_context_len), float(scale), int(partition_size), _DTYPE[query.dtype],
-        _DTYPE[key_cache.dtype], _ptr(workspace), ws_bytes, _stream(stream)))
+    args = [_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(k_scale), _ptr(v_scale),
+            _ptr(block_tables), _ptr(context_lens), B, hq, hkv, d, nb, block_tables.shape[1],
+            int(max_context_len), float(scale), int(partition_size), _DTYPE[query.dtype],
+            _DTYPE[key_cache.dtype], _ptr(workspace), ws_bytes, _stream(stream)]
+    lib = load_library()
+    _check(lib.pa_decode(*args) if window is None else lib.pa_decode_sliding(*args, window))
     return out

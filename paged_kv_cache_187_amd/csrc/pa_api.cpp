@@ -73,6 +73,68 @@ pa_status from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; 
 
 }  // namespace
 
+namespace {
+
+pa_status decode_impl(void* out, const void* query, const void* key_cache, const void* value_cache,
+                    const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                    const int32_t* context_lens, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                    int32_t head_dim, int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                    float scale, int32_t partition_size, int32_t q_dtype, int32_t cache_dtype, void* workspace,
+                    size_t workspace_bytes, void* stream, int32_t window) {
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 ||
+        num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || num_heads > 65536)
+        return PA_ERR_SHAPE;
+    if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+    if (!is16(q_dtype)) return PA_ERR_DTYPE;
+    const bool fp8 = cache_dtype == PA_FP8_E4M3;
+    if (!fp8 && cache_dtype != q_dtype) return PA_ERR_DTYPE;
+    if (!std::isfinite(scale) || window < 0) return PA_ERR_SHAPE;
+    const Plan pl = make_plan(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, partition_size);
+    if (!pl.ok) return PA_ERR_SHAPE;
+    const size_t need = workspace_size(pl, head_dim);
+    if (num_seqs == 0) return PA_OK;
+    if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens) return PA_ERR_NULL;
+    if (fp8 && (!k_scale || !v_scale)) return PA_ERR_NULL;
+    if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+    if (!aligned(out, 16) || !aligned(query, 16) || !aligned(key_cache, 16) || !aligned(value_cache, 16) ||
+        !aligned(block_tables, 4) || !aligned(context_lens, 4) || (need > 0 && !aligned(workspace, 16)) ||
+        (fp8 && (!aligned(k_scale, 16) || !aligned(v_scale, 16))))
+        return PA_ERR_ALIGN;
+
+    pa::DecodeParams p{};
+    p.out = out;
+    p.query = query;
+    p.key_cache = key_cache;
+    p.value_cache = value_cache;
+    p.k_scale = fp8 ? k_scale : nullptr;
+    p.v_scale = fp8 ? v_scale : nullptr;
+    p.block_tables = block_tables;
+    p.context_lens = context_lens;
+    if (need > 0) {
+        p.ws_acc = (float*)workspace;
+        p.ws_ml = p.ws_acc + (size_t)pl.slots * pl.hpw * head_dim;
+    }
+    p.num_blocks = num_blocks;
+    p.B = num_seqs;
+    p.Hq = num_heads;
+    p.Hkv = num_kv_heads;
+    p.max_blocks = max_blocks_per_seq;
+    const int64_t table_tokens = (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE;
+    p.ctx_limit = (int32_t)(table_tokens < max_context_len ? table_tokens : max_context_len);
+    p.balanced = pl.balanced ? 1 : 0;
+    p.NP = (int32_t)pl.np;
+    p.part_blocks = (int32_t)(pl.part / PA_BLOCK_SIZE);
+    p.groups = (int32_t)pl.groups;
+    p.hpw = (int32_t)pl.hpw;
+    p.mfma = pl.mfma ? 1 : 0;
+    p.num_waves = (int32_t)pl.waves;
+    p.window = window;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    return from_hip(pa::launch_decode(p, head_dim, q_dtype, cache_dtype, (hipStream_t)stream));
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* pa_status_string(int32_t status) {
@@ -157,55 +219,21 @@ pa_status pa_decode(void* out, const void* query, const void* key_cache, const v
                     int32_t head_dim, int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
                     float scale, int32_t partition_size, int32_t q_dtype, int32_t cache_dtype, void* workspace,
                     size_t workspace_bytes, void* stream) {
-    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 ||
-        num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || num_heads > 65536)
-        return PA_ERR_SHAPE;
-    if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
-    if (!is16(q_dtype)) return PA_ERR_DTYPE;
-    const bool fp8 = cache_dtype == PA_FP8_E4M3;
-    if (!fp8 && cache_dtype != q_dtype) return PA_ERR_DTYPE;
-    if (!std::isfinite(scale)) return PA_ERR_SHAPE;
-    const Plan pl = make_plan(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, partition_size);
-    if (!pl.ok) return PA_ERR_SHAPE;
-    const size_t need = workspace_size(pl, head_dim);
-    if (num_seqs == 0) return PA_OK;
-    if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens) return PA_ERR_NULL;
-    if (fp8 && (!k_scale || !v_scale)) return PA_ERR_NULL;
-    if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
-    if (!aligned(out, 16) || !aligned(query, 16) || !aligned(key_cache, 16) || !aligned(value_cache, 16) ||
-        !aligned(block_tables, 4) || !aligned(context_lens, 4) || (need > 0 && !aligned(workspace, 16)) ||
-        (fp8 && (!aligned(k_scale, 16) || !aligned(v_scale, 16))))
-        return PA_ERR_ALIGN;
+    return decode_impl(out, query, key_cache, value_cache, k_scale, v_scale, block_tables, context_lens, num_seqs,
+                       num_heads, num_kv_heads, head_dim, num_blocks, max_blocks_per_seq, max_context_len, scale,
+                       partition_size, q_dtype, cache_dtype, workspace, workspace_bytes, stream, 0);
+}
 
-    pa::DecodeParams p{};
-    p.out = out;
-    p.query = query;
-    p.key_cache = key_cache;
-    p.value_cache = value_cache;
-    p.k_scale = fp8 ? k_scale : nullptr;
-    p.v_scale = fp8 ? v_scale : nullptr;
-    p.block_tables = block_tables;
-    p.context_lens = context_lens;
-    if (need > 0) {
-        p.ws_acc = (float*)workspace;
-        p.ws_ml = p.ws_acc + (size_t)pl.slots * pl.hpw * head_dim;
-    }
-    p.num_blocks = num_blocks;
-    p.B = num_seqs;
-    p.Hq = num_heads;
-    p.Hkv = num_kv_heads;
-    p.max_blocks = max_blocks_per_seq;
-    const int64_t table_tokens = (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE;
-    p.ctx_limit = (int32_t)(table_tokens < max_context_len ? table_tokens : max_context_len);
-    p.balanced = pl.balanced ? 1 : 0;
-    p.NP = (int32_t)pl.np;
-    p.part_blocks = (int32_t)(pl.part / PA_BLOCK_SIZE);
-    p.groups = (int32_t)pl.groups;
-    p.hpw = (int32_t)pl.hpw;
-    p.mfma = pl.mfma ? 1 : 0;
-    p.num_waves = (int32_t)pl.waves;
-    p.scale_log2 = scale * 1.4426950408889634f;
-    return from_hip(pa::launch_decode(p, head_dim, q_dtype, cache_dtype, (hipStream_t)stream));
+pa_status pa_decode_sliding(void* out, const void* query, const void* key_cache, const void* value_cache,
+                            const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                            const int32_t* context_lens, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int64_t num_blocks, int32_t max_blocks_per_seq,
+                            int32_t max_context_len, float scale, int32_t partition_size, int32_t q_dtype,
+                            int32_t cache_dtype, void* workspace, size_t workspace_bytes, void* stream,
+                            int32_t sliding_window) {
+    return decode_impl(out, query, key_cache, value_cache, k_scale, v_scale, block_tables, context_lens, num_seqs,
+                       num_heads, num_kv_heads, head_dim, num_blocks, max_blocks_per_seq, max_context_len, scale,
+                       partition_size, q_dtype, cache_dtype, workspace, workspace_bytes, stream, sliding_window);
 }
 
 }  // extern "C"

@@ -64,8 +64,17 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ int seq_len(const DecodeParams& p, int b) { return clamp_len(p.context_lens[b], p.ctx_limit); }
 
+// First token a query attends to: with a sliding window of W tokens only the last
+// W of the L tokens count ("LLM推理引擎深度实战：…", §9.2 names sliding-window attention).
+__device__ __forceinline__ int first_token(const DecodeParams& p, int L) {
+    return (p.window > 0 && L > p.window) ? L - p.window : 0;
+}
+
+// Blocks of sequence b that hold tokens the query attends to ("in play"): from the
+// block of its first attended token to its last block.
 __device__ __forceinline__ int seq_blocks(const DecodeParams& p, int b) {
-    return (seq_len(p, b) + kBlockSize - 1) / kBlockSize;
+    const int L = seq_len(p, b);
+    return L > 0 ? (L + kBlockSize - 1) / kBlockSize - first_token(p, L) / kBlockSize : 0;
 }
 
 // Inclusive prefix sum over the 64 lanes of the wave.
@@ -212,7 +221,7 @@ struct Buf {
     float ks[Layout<CT, D>::LPB], vs[Layout<CT, D>::LPB];
 };
 static __device__ __forceinline__ void run(const DecodeParams& p, int lane, int b, int hg, int jb, int je,
-                                           int nblk, int L, int64_t slot) {
+                                           int jfirst, int nblk, int lo, int L, int64_t slot) {
     using Ly = Layout<CT, D>;
     constexpr int EB = Ly::EB, EPL = Ly::EPL, TPL = Ly::TPL, ROWS = Ly::ROWS, LPB = Ly::LPB;
     constexpr bool kFp8 = EB == 1;
@@ -309,7 +318,10 @@ static __device__ __forceinline__ void run(const DecodeParams& p, int lane, int 
         const float(&vsc)[LPB] = bf.vs;
         bool valid[LPB];
 #pragma unroll
-        for (int i = 0; i < LPB; ++i) valid[i] = j * kBlockSize + i * ROWS + row < L;
+        for (int i = 0; i < LPB; ++i) {
+            const int t = j * kBlockSize + i * ROWS + row;
+            valid[i] = t >= lo && t < L;
+        }
 
         float s[LPB][HPW];   // scores in log2 units
 #pragma unroll
@@ -394,7 +406,7 @@ static __device__ __forceinline__ void run(const DecodeParams& p, int lane, int 
 
     // Merge the ROWS row states (lanes with equal `chunk`); afterwards every row holds the
     // segment's result and the TPL lanes of row 0 write it.
-    const bool whole = jb == 0 && je == nblk;
+    const bool whole = jb == jfirst && je == nblk;
     const int64_t out_row = (int64_t)b * p.Hq + h0;
 #pragma unroll
     for (int h = 0; h < HPW; ++h) {
@@ -520,7 +532,7 @@ struct MfmaSegment {
     }
 
     static __device__ __forceinline__ void run(const DecodeParams& p, int lane, int b, int hg, int jb, int je,
-                                               int nblk, int L, int64_t slot) {
+                                               int jfirst, int nblk, int lo, int L, int64_t slot) {
         const int G = p.hpw;
         const int h0 = hg * G;
         const int hk = h0 / (p.Hq / p.Hkv);
@@ -595,7 +607,8 @@ struct MfmaSegment {
             bool valid[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                valid[r] = j * kBlockSize + 4 * g + r < L;
+                const int t = j * kBlockSize + 4 * g + r;
+                valid[r] = t >= lo && t < L;
                 const float f = kFp8 ? p.scale_log2 * ksc[r] : p.scale_log2;
                 sc[r] = valid[r] ? S[r] * f : kNegInf;
             }
@@ -664,7 +677,7 @@ struct MfmaSegment {
         // Totals per head (lane groups hold disjoint tokens), then per output row 4g + r.
         float ltot = lsum + __shfl_xor(lsum, 16);
         ltot += __shfl_xor(ltot, 32);
-        const bool whole = jb == 0 && je == nblk;
+        const bool whole = jb == jfirst && je == nblk;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int head = 4 * g + r;
@@ -710,12 +723,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeParams p) 
         const int s = w / p.NP;
         const int hg = s % p.groups;
         const int b = s / p.groups;
+        // Partitions cover the blocks in play, j0 .. nblk - 1.
         const int L = seq_len(p, b);
+        const int lo = first_token(p, L);
+        const int j0 = lo / kBlockSize;
         const int nblk = (L + kBlockSize - 1) / kBlockSize;
-        const int jb = part * p.part_blocks;
+        const int jb = j0 + part * p.part_blocks;
         if (jb >= nblk && !(part == 0 && nblk == 0)) return;   // L == 0: partition 0 writes zeros
         const int je = min(nblk, jb + p.part_blocks);
-        Segment::run(p, lane, b, hg, jb, je, nblk, L, (int64_t)s * p.NP + part);
+        Segment::run(p, lane, b, hg, jb, je, j0, nblk, lo, L, (int64_t)s * p.NP + part);
         return;
     }
 
@@ -725,13 +741,18 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeParams p) 
     int pos = rg.begin(w);
     const int pos_end = rg.end(w);
     while (pos < pos_end) {
+        // Position offsets count the blocks in play of (sequence, head group), which start
+        // at logical block j0.
         const SeqPos sp = locate(p, st, lane, pos);
         const int off = pos - p.groups * sp.start;
         const int hg = off / sp.nblk;
-        const int jb = off % sp.nblk;
-        const int je = min(sp.nblk, jb + (pos_end - pos));
+        const int L = seq_len(p, sp.b);
+        const int lo = first_token(p, L);
+        const int j0 = lo / kBlockSize;
+        const int jb = j0 + off % sp.nblk;
+        const int je = min(j0 + sp.nblk, jb + (pos_end - pos));
         const int s = sp.b * p.groups + hg;
-        Segment::run(p, lane, sp.b, hg, jb, je, sp.nblk, seq_len(p, sp.b), (int64_t)w + s);
+        Segment::run(p, lane, sp.b, hg, jb, je, j0, j0 + sp.nblk, lo, L, (int64_t)w + s);
         pos += je - jb;
     }
 }

@@ -30,6 +30,7 @@ struct DecodeParams {
     int32_t hpw;               // query heads per wave (all share one KV head)
     int32_t mfma;              // 1: matrix-core path (hpw <= 16 rows of a 16x16 tile)
     int32_t num_waves;         // waves in the grid
+    int32_t window;            // sliding window in tokens (0: attend to the whole context)
     float scale_log2;          // softmax scale * log2(e)
 };
 

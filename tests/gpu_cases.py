@@ -63,11 +63,11 @@ def oracle_caches(wh):
     return kc, vc, None, None
 
 
-def oracle_decode(wh, caches):
+def oracle_decode(wh, caches, window=0):
     kc, vc, ks, vs = caches
     cfg = wh.cfg
     return oracle.paged_decode(bits_np(wh.query), kc, vc, wh.tables_np, wh.lens_np, cfg.scale, cfg.q_dtype,
-                               cfg.cache_dtype, ks, vs)
+                               cfg.cache_dtype, ks, vs, window=window)
 
 
 def errors(out_gpu, ref):

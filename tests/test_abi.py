@@ -36,7 +36,7 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert _declared() == ["pa_append_kv", "pa_copy_blocks", "pa_decode", "pa_decode_partition_size",
-                           "pa_decode_workspace_bytes", "pa_status_string"]
+                           "pa_decode_sliding", "pa_decode_workspace_bytes", "pa_status_string"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -79,6 +79,22 @@ def _decode(lib, **kw):
     return lib.pa_decode(a["out"], a["query"], a["key_cache"], a["value_cache"], a["k_scale"], a["v_scale"],
                          a["block_tables"], a["context_lens"], a["B"], a["Hq"], a["Hkv"], a["D"], a["nb"],
                          a["mb"], a["maxL"], a["scale"], a["part"], a["qd"], a["cd"], a["ws"], a["wsb"], None)
+
+
+def test_sliding_decode_host_checks(lib):
+    def sl(window, **kw):
+        a = dict(out=FAKE, query=FAKE, key_cache=FAKE, value_cache=FAKE, k_scale=None, v_scale=None,
+                 block_tables=FAKE, context_lens=FAKE, B=2, Hq=8, Hkv=2, D=128, nb=10, mb=4, maxL=64,
+                 scale=0.1, part=0, qd=F16, cd=F16, ws=None, wsb=0)
+        a.update(kw)
+        return lib.pa_decode_sliding(a["out"], a["query"], a["key_cache"], a["value_cache"], a["k_scale"],
+                                     a["v_scale"], a["block_tables"], a["context_lens"], a["B"], a["Hq"], a["Hkv"],
+                                     a["D"], a["nb"], a["mb"], a["maxL"], a["scale"], a["part"], a["qd"], a["cd"],
+                                     a["ws"], a["wsb"], None, window)
+    assert sl(-1) == SHAPE
+    assert sl(16, out=None) == NULL
+    assert sl(16) == WS                                      # the balanced split needs a workspace
+    assert sl(16, B=0) == OK
 
 
 def test_decode_host_checks(lib):
