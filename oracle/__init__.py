@@ -18,7 +18,8 @@ package's own codecs), written to be checked by eye against the pages:
 * "大模型推理引擎优化：KV Cache 与连续批处理" (devpress.csdn.net), §2.1 and §2.2: every
   decode step attends over the K/V of all previous tokens; blocks hold 16
   tokens and are allocated on demand.  §4.2: a block that several sequences
-  share is copied before one of them writes into it (copy-on-write).
+  share is copied before one of them writes into it (copy-on-write).  The
+  ybb.press page §3.2: preempted requests' pages go to CPU memory and come back.
 
 Pins (tests marked ``not gpu`` under ``tests/``) tie each function to something
 other than itself: brute-force dense attention and torch's
@@ -37,7 +38,7 @@ from .codecs import (  # noqa: F401
     decode_bits,
 )
 from .kv_append import append_kv, quantize_tokens_e4m3, append_kv_e4m3  # noqa: F401
-from .block_copy import copy_blocks  # noqa: F401
+from .block_copy import copy_blocks, swap_blocks  # noqa: F401
 from .paged_attention import (  # noqa: F401
     attend,
     attention_weights,

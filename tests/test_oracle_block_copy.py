@@ -57,3 +57,33 @@ def test_fp8_scales_travel_with_their_blocks():
     assert np.array_equal(ks2[5], ks[0]) and np.array_equal(vs2[5], vs[0])
     assert np.array_equal(np.delete(ks2, 5, 0), np.delete(ks, 5, 0))
     assert np.array_equal(k2[5], kc[0]) and np.array_equal(v2[5], vc[0])
+
+
+def test_swap_matches_element_loop_across_pools():
+    rng = np.random.default_rng(3)
+    src = (_pool(rng, nb=9), _pool(rng, nb=9), None, None)
+    dst = (_pool(rng, nb=5), _pool(rng, nb=5), None, None)
+    pairs = np.array([[8, 0], [2, 4], [9, 1], [3, -1], [0, 5], [4, 3]], dtype=np.int64)
+    k2, v2, _, _ = oracle.swap_blocks(src, dst, pairs)
+    want_k, want_v = dst[0].copy(), dst[1].copy()
+    for s_, d_ in pairs.tolist():
+        if 0 <= s_ < 9 and 0 <= d_ < 5:
+            for o in range(16):
+                for h in range(src[0].shape[2]):
+                    for e in range(src[0].shape[3]):
+                        want_k[d_, o, h, e] = src[0][s_, o, h, e]
+                        want_v[d_, o, h, e] = src[1][s_, o, h, e]
+    assert np.array_equal(k2, want_k) and np.array_equal(v2, want_v)
+
+
+def test_swap_out_then_in_restores_the_blocks_and_their_scales():
+    rng = np.random.default_rng(4)
+    gpu = (_pool(rng, nb=12, dtype=np.uint8), _pool(rng, nb=12, dtype=np.uint8),
+           rng.random((12, 16)).astype(np.float32), rng.random((12, 16)).astype(np.float32))
+    host = tuple(np.zeros((4,) + a.shape[1:], a.dtype) for a in gpu)
+    out_pairs = np.array([[7, 0], [2, 1], [11, 2]])
+    host2 = oracle.swap_blocks(gpu, host, out_pairs)
+    back = oracle.swap_blocks(host2, gpu, np.array([[0, 3], [1, 4], [2, 5]]))
+    for a, b in zip(gpu, back):
+        for s_, d_ in [(7, 3), (2, 4), (11, 5)]:
+            assert np.array_equal(b[d_], a[s_])
