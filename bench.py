@@ -228,6 +228,42 @@ def time_copy_blocks(steps, warmup, pairs, num_blocks=4096, replicas=2):
             "frac_of_peak": round(moved / (mean * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def time_swap(steps, warmup, pairs=256, num_blocks=1024):
+    """pa_swap_blocks between a GPU pool and a pinned host pool, llama7b-shaped blocks.
+
+    Swap-out copies `pairs` random GPU blocks (K and V, 128 KiB each) to the host pool and swap-in
+    copies them back to other GPU blocks; bytes moved per call = pairs x 2 x 128 KiB over PCIe.
+    """
+    import numpy as np
+    import torch
+    import paged_kv_cache_187_amd as pa
+
+    hkv, d = 32, 128
+    gpu = (torch.empty(num_blocks, 16, hkv, d, dtype=torch.float16, device="cuda").normal_(),
+           torch.empty(num_blocks, 16, hkv, d, dtype=torch.float16, device="cuda").normal_(), None, None)
+    host = (torch.zeros(pairs, 16, hkv, d, dtype=torch.float16, pin_memory=True),
+            torch.zeros(pairs, 16, hkv, d, dtype=torch.float16, pin_memory=True), None, None)
+    ids = np.random.default_rng(6).permutation(num_blocks)
+    out_map = torch.from_numpy(np.stack([ids[:pairs], np.arange(pairs)], 1).astype(np.int64)).cuda()
+    in_map = torch.from_numpy(np.stack([np.arange(pairs), ids[pairs:2 * pairs]], 1).astype(np.int64)).cuda()
+    moved = pairs * 2 * 16 * hkv * d * 2
+    res = {"pairs": pairs, "bytes_per_call": moved}
+    stream = torch.cuda.current_stream()
+    for name, src, dst, m in (("swap_out", gpu, host, out_map), ("swap_in", host, gpu, in_map)):
+        for _ in range(warmup):
+            pa.pa_swap_blocks(src, dst, m)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in ev:
+            a.record(stream)
+            pa.pa_swap_blocks(src, dst, m)
+            b.record(stream)
+        torch.cuda.synchronize()
+        us = sum(a.elapsed_time(b) for a, b in ev) * 1e3 / steps
+        res[name] = {"us_mean": round(us, 1), "GBs": round(moved / (us * 1e-6) / 1e9, 1)}
+    return res
+
+
 def cpu_baseline(w, host, min_seconds):
     """The float64 oracle on the host, on the same workload (pre-step state), single-threaded."""
     import numpy as np
@@ -291,7 +327,7 @@ def main():
                     "and decode instead of launching from Python (slower on ROCm 7 for this two-launch step)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (5 times), to scale rocprofv3 FETCH_SIZE/WRITE_SIZE")
-    ap.add_argument("--no-copy", action="store_true", help="skip the pa_copy_blocks measurement")
+    ap.add_argument("--no-copy", action="store_true", help="skip the pa_copy_blocks / pa_swap_blocks measurements")
     ap.add_argument("--window", type=int, default=512,
                     help="sliding window (tokens) of the extra pa_decode_sliding line on the main workload; 0 = skip")
     ap.add_argument("--partition-size", type=int, default=None,
@@ -343,6 +379,7 @@ def main():
     if not args.no_copy:
         also["copy_blocks"] = {"bandwidth": time_copy_blocks(args.steps, args.warmup, 1024),
                                "copy_on_write_64_pairs": time_copy_blocks(args.steps, args.warmup, 64)}
+        also["swap_blocks"] = time_swap(min(args.steps, 50), min(args.warmup, 5))
         torch.cuda.empty_cache()
 
     result = {

@@ -21,6 +21,10 @@
  *    block manager takes before a sequence writes into a block that other
  *    sequences share ("大模型推理引擎优化：…", §4.2; "LLM推理引擎深度实战：…", §2.2).
  *
+ *  - pa_swap_blocks: the same copy between two pools, one of which may be
+ *    pinned host memory: a preempted request's blocks go out to CPU memory and
+ *    come back when it resumes ("LLM推理引擎深度实战：…", §3.2).
+ *
  * Layouts (all row-major, contiguous, little-endian):
  *   query        [num_seqs, num_heads, head_dim]                 q_dtype
  *   out          [num_seqs, num_heads, head_dim]                 q_dtype
@@ -73,7 +77,8 @@ typedef enum pa_status {
     PA_ERR_UNSUPPORTED = 4, /* head_dim or head grouping the kernels do not cover */
     PA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required        */
     PA_ERR_HIP = 6,         /* the HIP runtime reported an error                 */
-    PA_ERR_ALIGN = 7        /* a buffer is not 16-byte aligned                   */
+    PA_ERR_ALIGN = 7,       /* a buffer is not 16-byte aligned                   */
+    PA_ERR_ADDRESS = 8      /* a buffer is not addressable by the GPU            */
 } pa_status;
 
 typedef enum pa_dtype {
@@ -132,6 +137,32 @@ pa_status pa_copy_blocks(void *key_cache, void *value_cache,
                          float *k_scale, float *v_scale,
                          const int64_t *block_mapping, int64_t num_pairs,
                          int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                         int32_t cache_dtype, void *stream);
+
+/*
+ * pa_swap_blocks - for every pair i < num_pairs with (src, dst) =
+ * (block_mapping[2 i], block_mapping[2 i + 1]): copy block src of the source
+ * pools (src_key, src_value and, for an FP8 cache, src_k_scale / src_v_scale)
+ * to block dst of the destination pools, bit for bit.
+ *
+ * Either side may be pinned host memory the GPU can address (hipHostMalloc'd,
+ * e.g. a torch tensor created with pin_memory=True); the copy then crosses
+ * PCIe.  Every buffer is checked on the host with hipPointerGetAttributes
+ * (which does not synchronise): one that the GPU cannot reach at the same
+ * address returns PA_ERR_ADDRESS and nothing is launched.  block_mapping lives in device memory (or pinned host memory).  Pairs
+ * with src outside [0, src_num_blocks) or dst outside [0, dst_num_blocks) are
+ * skipped; the destinations of one call must be distinct.  Both sides have
+ * the layout of key_cache / value_cache ([*_num_blocks, 16, num_kv_heads,
+ * head_dim], cache_dtype) and of the scales; alignment as pa_copy_blocks.
+ */
+pa_status pa_swap_blocks(const void *src_key, const void *src_value,
+                         const float *src_k_scale, const float *src_v_scale,
+                         int64_t src_num_blocks,
+                         void *dst_key, void *dst_value,
+                         float *dst_k_scale, float *dst_v_scale,
+                         int64_t dst_num_blocks,
+                         const int64_t *block_mapping, int64_t num_pairs,
+                         int32_t num_kv_heads, int32_t head_dim,
                          int32_t cache_dtype, void *stream);
 
 /*

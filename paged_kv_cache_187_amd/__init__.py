@@ -1,4 +1,4 @@
-"""gfx950 (MI355X) paged decode attention, slot-mapped KV append and copy-on-write block copy.
+"""gfx950 (MI355X) paged decode attention, slot-mapped KV append, block copy and swap.
 
 The work runs in hand-written HIP kernels behind the C ABI declared in
 ``include/pagedattn.h`` (``libpagedattn.so``, built in-tree by
@@ -19,4 +19,5 @@ from .binding import (  # noqa: F401
     pa_copy_blocks,
     pa_decode,
     pa_decode_sliding,
+    pa_swap_blocks,
 )

@@ -46,6 +46,8 @@ def load_library(path=LIB_PATH):
     lib.pa_append_kv.restype = i32
     lib.pa_copy_blocks.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i64, i32, vp]
     lib.pa_copy_blocks.restype = i32
+    lib.pa_swap_blocks.argtypes = [vp, vp, vp, vp, i64, vp, vp, vp, vp, i64, vp, i64, i32, i32, i32, vp]
+    lib.pa_swap_blocks.restype = i32
     lib.pa_decode_partition_size.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.pa_decode_partition_size.restype = i32
     lib.pa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
@@ -77,6 +79,16 @@ def _on_gpu(*tensors):
             continue
         if not t.is_cuda:
             raise ValueError("paged attention tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("paged attention tensors must be contiguous")
+
+
+def _gpu_or_pinned(*tensors):
+    for t in tensors:
+        if t is None:
+            continue
+        if not (t.is_cuda or t.is_pinned()):
+            raise ValueError("swap pools must live on the GPU or in pinned host memory")
         if not t.is_contiguous():
             raise ValueError("paged attention tensors must be contiguous")
 
@@ -122,6 +134,27 @@ def pa_copy_blocks(key_cache, value_cache, block_mapping, k_scale=None, v_scale=
     _check(load_library().pa_copy_blocks(
         _ptr(key_cache), _ptr(value_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_mapping),
         block_mapping.shape[0], hkv, d, nb, cdt, _stream(stream)))
+
+
+def pa_swap_blocks(src, dst, block_mapping, stream=None):
+    """Copy block src of pools ``src`` to block dst of pools ``dst`` for block_mapping [n, 2] int64 pairs.
+
+    src, dst: (key_cache, value_cache, k_scale, v_scale) tuples (scales None unless FP8) on the GPU
+    or in pinned host memory (swap-out: GPU -> pinned host; swap-in: pinned host -> GPU).
+    """
+    sk, sv, sks, svs = src
+    dk, dv, dks, dvs = dst
+    _gpu_or_pinned(sk, sv, sks, svs, dk, dv, dks, dvs)
+    _on_gpu(block_mapping)
+    if sk.shape[1:] != dk.shape[1:] or sv.shape != sk.shape or dv.shape != dk.shape or sk.dtype != dk.dtype or \
+            sk.shape[1] != BLOCK_SIZE or block_mapping.dtype != torch.int64 or block_mapping.dim() != 2 or \
+            block_mapping.shape[1] != 2:
+        raise ValueError("inconsistent shapes for pa_swap_blocks")
+    cdt = _DTYPE[sk.dtype]
+    _, _, hkv, d = sk.shape
+    _check(load_library().pa_swap_blocks(
+        _ptr(sk), _ptr(sv), _ptr(sks), _ptr(svs), sk.shape[0], _ptr(dk), _ptr(dv), _ptr(dks), _ptr(dvs),
+        dk.shape[0], _ptr(block_mapping), block_mapping.shape[0], hkv, d, cdt, _stream(stream)))
 
 
 def decode_partition_size(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, partition_size=0):

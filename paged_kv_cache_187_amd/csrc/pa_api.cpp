@@ -71,6 +71,42 @@ bool is16(int32_t d) { return d == PA_F16 || d == PA_BF16; }
 
 pa_status from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
 
+// Host checks shared by the block copies (one pool's pointers and sizes).
+pa_status check_copy(const void* key, const void* value, const float* k_scale, const float* v_scale,
+                     const int64_t* mapping, int64_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                     int64_t num_blocks, int32_t cache_dtype) {
+    if (num_pairs < 0 || num_pairs > ((int64_t)1 << 31) - 1 || num_kv_heads <= 0 || num_kv_heads > 4096 ||
+        num_blocks <= 0)
+        return PA_ERR_SHAPE;
+    if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+    const bool fp8 = cache_dtype == PA_FP8_E4M3;
+    if (!fp8 && !is16(cache_dtype)) return PA_ERR_DTYPE;
+    if (num_pairs == 0) return PA_OK;
+    if (!key || !value || !mapping) return PA_ERR_NULL;
+    if (fp8 && (!k_scale || !v_scale)) return PA_ERR_NULL;
+    if (!aligned(key, 16) || !aligned(value, 16) || !aligned(mapping, 8) ||
+        (fp8 && (!aligned(k_scale, 4) || !aligned(v_scale, 4))))
+        return PA_ERR_ALIGN;
+    return PA_OK;
+}
+
+// True when the GPU reaches `p` at the same address: device memory, or host memory
+// pinned and mapped into the GPU's address space.  A failed query leaves no error
+// behind for the launch check that follows.
+bool gpu_addressable(const void* p) {
+    if (p == nullptr) return true;
+    hipPointerAttribute_t a{};
+    if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    return a.devicePointer == p;
+}
+
+int64_t block_bytes(int32_t num_kv_heads, int32_t head_dim, bool fp8) {
+    return (int64_t)PA_BLOCK_SIZE * num_kv_heads * head_dim * (fp8 ? 1 : 2);
+}
+
 }  // namespace
 
 namespace {
@@ -147,6 +183,7 @@ const char* pa_status_string(int32_t status) {
         case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
         case PA_ERR_HIP: return "PA_ERR_HIP: the HIP runtime reported an error";
         case PA_ERR_ALIGN: return "PA_ERR_ALIGN: a buffer is not 16-byte aligned";
+        case PA_ERR_ADDRESS: return "PA_ERR_ADDRESS: a buffer is not addressable by the GPU";
         default: return "unknown pa_status";
     }
 }
@@ -182,21 +219,38 @@ pa_status pa_append_kv(const void* key, const void* value, void* key_cache, void
 pa_status pa_copy_blocks(void* key_cache, void* value_cache, float* k_scale, float* v_scale,
                          const int64_t* block_mapping, int64_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
                          int64_t num_blocks, int32_t cache_dtype, void* stream) {
-    if (num_pairs < 0 || num_pairs > ((int64_t)1 << 31) - 1 || num_kv_heads <= 0 || num_kv_heads > 4096 ||
-        num_blocks <= 0)
-        return PA_ERR_SHAPE;
-    if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+    const pa_status st = check_copy(key_cache, value_cache, k_scale, v_scale, block_mapping, num_pairs, num_kv_heads,
+                                    head_dim, num_blocks, cache_dtype);
+    if (st != PA_OK || num_pairs == 0) return st;
     const bool fp8 = cache_dtype == PA_FP8_E4M3;
-    if (!fp8 && !is16(cache_dtype)) return PA_ERR_DTYPE;
-    if (num_pairs == 0) return PA_OK;
-    if (!key_cache || !value_cache || !block_mapping) return PA_ERR_NULL;
-    if (fp8 && (!k_scale || !v_scale)) return PA_ERR_NULL;
-    if (!aligned(key_cache, 16) || !aligned(value_cache, 16) || !aligned(block_mapping, 8) ||
-        (fp8 && (!aligned(k_scale, 4) || !aligned(v_scale, 4))))
-        return PA_ERR_ALIGN;
-    const int64_t block_bytes = (int64_t)PA_BLOCK_SIZE * num_kv_heads * head_dim * (fp8 ? 1 : 2);
     return from_hip(pa::launch_copy_blocks(key_cache, value_cache, fp8 ? k_scale : nullptr, fp8 ? v_scale : nullptr,
-                                           block_mapping, num_pairs, block_bytes, num_blocks, (hipStream_t)stream));
+                                           num_blocks, key_cache, value_cache, fp8 ? k_scale : nullptr,
+                                           fp8 ? v_scale : nullptr, num_blocks, true, block_mapping, num_pairs,
+                                           block_bytes(num_kv_heads, head_dim, fp8), (hipStream_t)stream));
+}
+
+pa_status pa_swap_blocks(const void* src_key, const void* src_value, const float* src_k_scale,
+                         const float* src_v_scale, int64_t src_num_blocks, void* dst_key, void* dst_value,
+                         float* dst_k_scale, float* dst_v_scale, int64_t dst_num_blocks,
+                         const int64_t* block_mapping, int64_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t cache_dtype, void* stream) {
+    pa_status st = check_copy(src_key, src_value, src_k_scale, src_v_scale, block_mapping, num_pairs, num_kv_heads,
+                              head_dim, src_num_blocks, cache_dtype);
+    if (st == PA_OK)
+        st = check_copy(dst_key, dst_value, dst_k_scale, dst_v_scale, block_mapping, num_pairs, num_kv_heads,
+                        head_dim, dst_num_blocks, cache_dtype);
+    if (st != PA_OK || num_pairs == 0) return st;
+    const bool fp8 = cache_dtype == PA_FP8_E4M3;
+    const void* bufs[] = {src_key, src_value, dst_key, dst_value, block_mapping,
+                          fp8 ? src_k_scale : nullptr, fp8 ? src_v_scale : nullptr,
+                          fp8 ? dst_k_scale : nullptr, fp8 ? dst_v_scale : nullptr};
+    for (const void* b : bufs)
+        if (!gpu_addressable(b)) return PA_ERR_ADDRESS;
+    return from_hip(pa::launch_copy_blocks(src_key, src_value, fp8 ? src_k_scale : nullptr,
+                                           fp8 ? src_v_scale : nullptr, src_num_blocks, dst_key, dst_value,
+                                           fp8 ? dst_k_scale : nullptr, fp8 ? dst_v_scale : nullptr, dst_num_blocks,
+                                           false, block_mapping, num_pairs, block_bytes(num_kv_heads, head_dim, fp8),
+                                           (hipStream_t)stream));
 }
 
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,

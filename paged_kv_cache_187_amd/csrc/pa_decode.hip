@@ -820,7 +820,7 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodePara
     const int64_t kstride = (int64_t)hpw * D;
 
     // The V sums of the first kPre partials are loaded together with the (m, l) pairs.
-    constexpr int kPre = 8;
+    constexpr int kPre = 16;
     float pre[kPre][EPT];
 #pragma unroll
     for (int k = 0; k < kPre; ++k)

@@ -42,11 +42,14 @@ hipError_t launch_append_fp8(const void* key, const void* value, void* key_cache
                              float* k_scale, float* v_scale, const int64_t* slots, int64_t num_tokens,
                              int32_t row_elems, int64_t num_slots, int src_kind, hipStream_t stream);
 
-// Whole-block copies of the K and V pools (and FP8 scales when k_scale is not null)
-// for (src, dst) pairs; block_bytes is the bytes of one block of one pool.
-hipError_t launch_copy_blocks(void* key_cache, void* value_cache, float* k_scale, float* v_scale,
-                              const int64_t* mapping, int64_t num_pairs, int64_t block_bytes, int64_t num_blocks,
-                              hipStream_t stream);
+// Whole-block copies from block src of the source pools to block dst of the destination
+// pools for (src, dst) pairs (FP8 scales too when the scale pointers are not null);
+// block_bytes is the bytes of one block of one pool.  same_pool: the pools are the same
+// buffers (pairs with src == dst are skipped).
+hipError_t launch_copy_blocks(const void* src_key, const void* src_value, const float* src_k_scale,
+                              const float* src_v_scale, int64_t src_blocks, void* dst_key, void* dst_value,
+                              float* dst_k_scale, float* dst_v_scale, int64_t dst_blocks, bool same_pool,
+                              const int64_t* mapping, int64_t num_pairs, int64_t block_bytes, hipStream_t stream);
 
 // Query heads of one KV head handled together by one wave, and whether that
 // wave uses the matrix cores.

@@ -91,3 +91,93 @@ def test_copy_on_write_then_append_then_decode():
     torch.cuda.synchronize()
     assert np.array_equal(bits_np(dk), okc) and np.array_equal(bits_np(dv), ovc)
     assert_close(out, ref, "bf16", "copy-on-write step")
+
+
+def _pinned_like(t, nb):
+    return torch.zeros((nb,) + tuple(t.shape[1:]), dtype=t.dtype, pin_memory=True)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8_e4m3"])
+def test_swap_out_and_in_bit_exact(dtype):
+    print(f"[case] swap out/in {dtype}", flush=True)
+    nb, hkv, d, n = 64, 8, 128, 12
+    g = torch.Generator().manual_seed(11)
+    if dtype == "fp8_e4m3":
+        kc = torch.randint(0, 256, (nb, 16, hkv, d), generator=g, dtype=torch.uint8)
+        vc = torch.randint(0, 256, (nb, 16, hkv, d), generator=g, dtype=torch.uint8)
+        ks, vs = torch.rand(nb, 16, generator=g), torch.rand(nb, 16, generator=g)
+    else:
+        kc = torch.randn(nb, 16, hkv, d, generator=g).to(torch.bfloat16)
+        vc = torch.randn(nb, 16, hkv, d, generator=g).to(torch.bfloat16)
+        ks = vs = None
+    gpu = tuple(None if t is None else t.cuda() for t in (kc, vc, ks, vs))
+    host = tuple(None if t is None else _pinned_like(t, n) for t in (kc, vc, ks, vs))
+    rng = np.random.default_rng(12)
+    out_pairs = np.stack([rng.permutation(nb)[:n], np.arange(n)], 1).astype(np.int64)
+    out_pairs = np.concatenate([out_pairs, [[nb, 0], [-1, 1], [0, n]]]).astype(np.int64)   # skipped pairs
+    pa.pa_swap_blocks(gpu, host, torch.from_numpy(out_pairs).cuda())
+    torch.cuda.synchronize()
+    want = oracle.swap_blocks(tuple(None if t is None else bits_np(t) if t.dtype != torch.float32 else t.numpy()
+                                    for t in (kc, vc, ks, vs)),
+                              tuple(None if t is None else np.zeros((n,) + tuple(t.shape[1:]), bits_np(t).dtype
+                                                                    if t.dtype != torch.float32 else np.float32)
+                                    for t in (kc, vc, ks, vs)), out_pairs)
+    for got, exp in zip(host, want):
+        if got is not None:
+            g_np = bits_np(got) if got.dtype != torch.float32 else got.numpy()
+            assert np.array_equal(g_np.view(np.uint8), exp.view(np.uint8))
+    # swap back into other GPU blocks
+    in_pairs = np.stack([np.arange(n), rng.permutation(nb)[:n]], 1).astype(np.int64)
+    gpu2 = tuple(None if t is None else torch.zeros_like(t) for t in gpu)
+    pa.pa_swap_blocks(host, gpu2, torch.from_numpy(in_pairs).cuda())
+    torch.cuda.synchronize()
+    for a, b in zip(gpu, gpu2):
+        if a is None:
+            continue
+        for (s_, _), (h_, d_) in zip(out_pairs[:n], in_pairs):
+            assert torch.equal(a[int(s_)].view(torch.uint8), b[int(d_)].view(torch.uint8))
+
+
+def test_preempt_and_resume_decode_is_bitwise_unchanged():
+    """Swap a sequence's blocks out to pinned host memory, wipe them, swap them back into other
+    free blocks and point its table there: the decode output is bitwise what it was."""
+    print("[case] preempt / resume", flush=True)
+    wh = synth.make_workload("tiny")
+    w = synth.make_workload("tiny", device="cuda")
+    pa.pa_append_kv(w.key_new, w.value_new, w.key_cache, w.value_cache, w.slot_mapping)
+    before = torch.empty_like(w.query)
+    pa.pa_decode(before, w.query, w.key_cache, w.value_cache, w.block_tables, w.context_lens, w.cfg.scale,
+                 w.max_context_len)
+    torch.cuda.synchronize()
+    b = 3                                        # the longest sequence (50 tokens, 4 blocks)
+    nblk = synth.blocks_for(int(wh.lens_np[b]))
+    own = wh.tables_np[b, :nblk].astype(np.int64)
+    used = set(wh.tables_np[np.arange(4)[:, None], :].ravel().tolist())
+    free = np.array([x for x in range(w.num_blocks) if x not in used][:nblk], dtype=np.int64)
+    host = (_pinned_like(w.key_cache, nblk), _pinned_like(w.value_cache, nblk), None, None)
+    pa.pa_swap_blocks((w.key_cache, w.value_cache, None, None), host,
+                      torch.from_numpy(np.stack([own, np.arange(nblk)], 1)).cuda())
+    torch.cuda.synchronize()
+    w.key_cache[torch.from_numpy(own).cuda()] = float("nan")    # the blocks go to other requests
+    w.value_cache[torch.from_numpy(own).cuda()] = float("nan")
+    pa.pa_swap_blocks(host, (w.key_cache, w.value_cache, None, None),
+                      torch.from_numpy(np.stack([np.arange(nblk), free], 1)).cuda())
+    tables = w.block_tables.clone()
+    tables[b, :nblk] = torch.from_numpy(free.astype(np.int32)).cuda()
+    after = torch.empty_like(w.query)
+    pa.pa_decode(after, w.query, w.key_cache, w.value_cache, tables, w.context_lens, w.cfg.scale,
+                 w.max_context_len)
+    torch.cuda.synchronize()
+    assert torch.equal(before.view(torch.int16), after.view(torch.int16))
+
+
+def test_swap_rejects_memory_the_gpu_cannot_address():
+    """A plain (unpinned) host buffer is refused on the host: nothing is launched."""
+    print("[case] swap address check", flush=True)
+    lib = pa.load_library()
+    kc = torch.zeros(4, 16, 1, 64, dtype=torch.bfloat16, device="cuda")
+    plain = np.zeros((4, 16, 1, 64), dtype=np.uint16)
+    mapping = torch.zeros(1, 2, dtype=torch.int64, device="cuda")
+    st = lib.pa_swap_blocks(kc.data_ptr(), kc.data_ptr(), None, None, 4, plain.ctypes.data, plain.ctypes.data,
+                            None, None, 4, mapping.data_ptr(), 1, 1, 64, 1, None)
+    assert st == 8    # PA_ERR_ADDRESS
