@@ -44,6 +44,7 @@ from .paged_attention import (  # noqa: F401
     attention_weights,
     gather_kv,
     paged_decode,
+    paged_decode_multi,
     paged_decode_one,
     partial_attend,
     merge_partials,

@@ -23,6 +23,14 @@ query head h:
 The gather into contiguous K/V is done first, then the attention, as the
 plain definition reads; numpy matrix products are the only library steps.
 
+Several new tokens per sequence ("LLM推理引擎深度实战：…", §6.1: the large model
+checks γ speculative tokens in one forward pass; "大模型推理引擎优化：…", §4.1: chunked
+prefill runs a long input a chunk at a time): with Q new tokens appended, the
+sequence holds L tokens and new token i (0 <= i < Q) sits at position
+L - Q + i.  Reading (causal attention, as the forward pass over those tokens
+computes): its query attends to tokens 0 .. L - Q + i, so new tokens see the
+cache and the new tokens before them, never those after.
+
 Sliding window ("LLM推理引擎深度实战：…", §9.2 names sliding-window attention, as in
 Mistral, among the long-context methods without defining it; the reading taken
 is the usual one): with a window of W > 0 tokens the query of a sequence of
@@ -105,6 +113,31 @@ def paged_decode(query, key_cache, value_cache, block_tables, context_lens, scal
         V = gather_kv(value_cache, block_tables[b], L, cache_dtype, v_scale)[lo:]
         for h in range(Hq):
             out[b, h] = attend(q[b, h], K[:, h // g, :], V[:, h // g, :], scale)
+    return out
+
+
+def paged_decode_multi(query, key_cache, value_cache, block_tables, context_lens, scale,
+                       q_dtype, cache_dtype, k_scale=None, v_scale=None):
+    """Paged attention of Q new tokens per sequence, causal within the new chunk.
+
+    query: [B, Q, Hq, D] bit patterns of ``q_dtype``; context_lens [B] count the Q new tokens.
+    Query i of sequence b attends to tokens 0 .. L_b - Q + i (zeros if that range is empty).
+    Returns float64 [B, Q, Hq, D].
+    """
+    q = decode_bits(query, q_dtype)
+    B, Q, Hq, D = q.shape
+    Hkv = key_cache.shape[2]
+    g = Hq // Hkv
+    out = np.zeros((B, Q, Hq, D), dtype=np.float64)
+    for b in range(B):
+        L = int(context_lens[b])
+        K = gather_kv(key_cache, block_tables[b], L, cache_dtype, k_scale)
+        V = gather_kv(value_cache, block_tables[b], L, cache_dtype, v_scale)
+        for i in range(Q):
+            last = L - Q + i                  # position of new token i; it sees tokens 0..last
+            n = max(0, last + 1)
+            for h in range(Hq):
+                out[b, i, h] = attend(q[b, i, h], K[:n, h // g, :], V[:n, h // g, :], scale)
     return out
 
 

@@ -278,3 +278,57 @@ def test_tokens_before_the_window_never_reach_the_output():
             vp[tables[b, t // BS], t % BS] = 0x7E00
     poisoned = oracle.paged_decode(q, kp, vp, tables, lens, 0.25, "f16", "f16", window=window)
     assert np.array_equal(clean, poisoned) and np.isfinite(poisoned).all()
+
+
+def _multi_case(seed, B=3, Q=4, Hq=4, Hkv=2, D=16, lens=(5, 16, 37), nb=12):
+    q1, kc, vc, tables, lens_np = _random_case(seed, B=B, Hq=Hq, Hkv=Hkv, D=D, lens=lens, nb=nb)
+    g = torch.Generator().manual_seed(seed + 100)
+    q = torch.randn(B, Q, Hq, D, generator=g).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    return q, kc, vc, tables, lens_np
+
+
+def test_multi_query_of_one_token_is_plain_decode():
+    q, kc, vc, tables, lens = _multi_case(51, Q=1)
+    multi = oracle.paged_decode_multi(q, kc, vc, tables, lens, 0.25, "f16", "f16")
+    single = oracle.paged_decode(q[:, 0], kc, vc, tables, lens, 0.25, "f16", "f16")
+    assert np.array_equal(multi[:, 0], single)
+
+
+def test_multi_query_causal_python_loops():
+    """Token i of the new chunk attends to positions 0 .. L - Q + i, written out directly."""
+    Q = 5
+    q, kc, vc, tables, lens = _multi_case(52, Q=Q, lens=(5, 16, 37))
+    out = oracle.paged_decode_multi(q, kc, vc, tables, lens, 0.3, "f16", "f16")
+    qd = oracle.decode_bits(q, "f16")
+    kd, vd = oracle.decode_bits(kc, "f16"), oracle.decode_bits(vc, "f16")
+    for b, L in enumerate(lens):
+        for i in range(Q):
+            toks = list(range(0, L - Q + i + 1))
+            for h in range(qd.shape[2]):
+                hk = h // 2
+                if not toks:
+                    assert np.array_equal(out[b, i, h], np.zeros(qd.shape[3]))
+                    continue
+                s = [0.3 * sum(qd[b, i, h, d] * kd[tables[b, t // BS], t % BS, hk, d] for d in range(qd.shape[3]))
+                     for t in toks]
+                mx = max(s)
+                e = [math.exp(x - mx) for x in s]
+                want = [sum(e[k] * vd[tables[b, t // BS], t % BS, hk, d] for k, t in enumerate(toks)) / sum(e)
+                        for d in range(qd.shape[3])]
+                assert np.allclose(out[b, i, h], want, rtol=1e-12, atol=1e-12)
+
+
+def test_multi_query_matches_torch_sdpa_with_offset_causal_mask():
+    """torch's scaled_dot_product_attention in float64 with the mask t <= L - Q + i."""
+    Q = 6
+    q, kc, vc, tables, lens = _multi_case(53, Q=Q, lens=(9, 16, 40), Hq=6, Hkv=3)
+    out = oracle.paged_decode_multi(q, kc, vc, tables, lens, 0.2, "f16", "f16")
+    qd = torch.from_numpy(oracle.decode_bits(q, "f16"))
+    for b, L in enumerate(lens):
+        K = torch.from_numpy(_dense_keys(kc, tables, b, L, "f16"))          # [L, Hkv, D]
+        V = torch.from_numpy(_dense_keys(vc, tables, b, L, "f16"))
+        mask = torch.tensor([[t <= L - Q + i for t in range(L)] for i in range(Q)])
+        for h in range(6):
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                qd[b, :, h][None], K[:, h // 2][None], V[:, h // 2][None], attn_mask=mask[None], scale=0.2)[0]
+            assert np.allclose(out[b, :, h], ref.numpy(), rtol=1e-12, atol=1e-12)
