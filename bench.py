@@ -101,7 +101,8 @@ def measured_traffic(workload):
     return int(fields["traffic_bytes_per_call"]) if h.hexdigest() == fields["kernel_sources_sha256"] else None
 
 
-def time_workload(name, steps, warmup, replicas, snapshot=False, partition_size=None, use_graphs=False, window=0):
+def time_workload(name, steps, warmup, replicas, snapshot=False, partition_size=None, use_graphs=False, window=0,
+                  q_len=1):
     import torch
     import paged_kv_cache_187_amd as pa
     import synth
@@ -123,15 +124,25 @@ def time_workload(name, steps, warmup, replicas, snapshot=False, partition_size=
         for r in range(replicas):
             pa.pa_append_kv(w.fill_key, w.fill_value, kcs[r], vcs[r], w.fill_slots, kss[r], vss[r])
     part = cfg.partition_size
-    ws = pa.alloc_workspace(w.query, cfg.num_kv_heads, w.max_context_len, part)
-    out = torch.empty_like(w.query)
     max_len = w.max_context_len
+    if q_len > 1:   # q_len new tokens per sequence: its last q_len cached positions
+        query = torch.randn(cfg.num_seqs, q_len, cfg.num_heads, cfg.head_dim, device="cuda").to(w.query.dtype)
+        n = pa.load_library().pa_decode_multi_workspace_bytes(cfg.num_seqs, q_len, cfg.num_heads, cfg.num_kv_heads,
+                                                             cfg.head_dim, max_len, part)
+        ws = torch.empty(n, dtype=torch.uint8, device="cuda") if n else None
+    else:
+        query = w.query
+        ws = pa.alloc_workspace(w.query, cfg.num_kv_heads, w.max_context_len, part)
+    out = torch.empty_like(query)
 
     def append(r):
         pa.pa_append_kv(w.key_new, w.value_new, kcs[r], vcs[r], w.slot_mapping, kss[r], vss[r])
 
     def decode(r):
-        if window > 0:
+        if q_len > 1:
+            pa.pa_decode_multi(out, query, kcs[r], vcs[r], w.block_tables, w.context_lens, cfg.scale, max_len,
+                               partition_size=part, k_scale=kss[r], v_scale=vss[r], workspace=ws)
+        elif window > 0:
             pa.pa_decode_sliding(out, w.query, kcs[r], vcs[r], w.block_tables, w.context_lens, cfg.scale, max_len,
                                  window, partition_size=part, k_scale=kss[r], v_scale=vss[r], workspace=ws)
         else:
@@ -185,7 +196,8 @@ def time_workload(name, steps, warmup, replicas, snapshot=False, partition_size=
         "decode_ms_p90": dec_ms[min(n - 1, (9 * n) // 10)],
         "partition_size": pa.decode_partition_size(cfg.num_seqs, cfg.num_heads, cfg.num_kv_heads, cfg.head_dim,
                                                    max_len, part),
-        "bytes": algorithmic_bytes(w, window),
+        "bytes": algorithmic_bytes(w, window) + (q_len - 1) * cfg.num_seqs * cfg.num_heads * cfg.head_dim * 2,
+        "q_len": q_len,
     }
 
 
@@ -302,7 +314,7 @@ def summarize(name, r):
     cfg = r["w"].cfg
     return {
         "workload": name,
-        "tokens_per_s": round(cfg.num_seqs / (r["ms_per_step"] * 1e-3), 1),
+        "tokens_per_s": round(cfg.num_seqs * r.get("q_len", 1) / (r["ms_per_step"] * 1e-3), 1),
         "ms_per_step": round(r["ms_per_step"], 5),
         "decode_us_mean": round(r["decode_ms_mean"] * 1e3, 2),
         "decode_us_p10_p50_p90": [round(r[k] * 1e3, 2) for k in ("decode_ms_p10", "decode_ms_p50", "decode_ms_p90")],
@@ -328,6 +340,8 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (5 times), to scale rocprofv3 FETCH_SIZE/WRITE_SIZE")
     ap.add_argument("--no-copy", action="store_true", help="skip the pa_copy_blocks / pa_swap_blocks measurements")
+    ap.add_argument("--multi", type=int, default=4,
+                    help="new tokens per sequence of the extra pa_decode_multi line on the main workload; <2 = skip")
     ap.add_argument("--window", type=int, default=512,
                     help="sliding window (tokens) of the extra pa_decode_sliding line on the main workload; 0 = skip")
     ap.add_argument("--partition-size", type=int, default=None,
@@ -369,6 +383,13 @@ def main():
         del r
         torch.cuda.empty_cache()
 
+    if args.multi > 1:
+        r = time_workload(args.workload, args.steps, args.warmup, args.replicas, partition_size=args.partition_size,
+                          use_graphs=args.graphs, q_len=args.multi)
+        also[f"{args.workload}_multi{args.multi}"] = summarize(args.workload, r)
+        also[f"{args.workload}_multi{args.multi}"]["q_len"] = args.multi
+        del r
+        torch.cuda.empty_cache()
     if args.window > 0:
         r = time_workload(args.workload, args.steps, args.warmup, args.replicas, partition_size=args.partition_size,
                           use_graphs=args.graphs, window=args.window)

@@ -15,7 +15,8 @@
  *    the sequence's page table; the kernel turns logical token indices into
  *    physical addresses, so the result is plain softmax attention over the
  *    tokens in logical order ("LLM推理引擎深度实战：…", §2.2 and §2.3);
- *    pa_decode_sliding restricts it to a sliding window of recent tokens.
+ *    pa_decode_sliding restricts it to a sliding window of recent tokens;
+ *    pa_decode_multi takes several new tokens per sequence (causal).
  *
  *  - pa_copy_blocks: copy whole physical blocks, the copy-on-write step the
  *    block manager takes before a sequence writes into a block that other
@@ -256,6 +257,37 @@ pa_status pa_decode_sliding(void *out, const void *query,
                             int32_t q_dtype, int32_t cache_dtype,
                             void *workspace, size_t workspace_bytes,
                             void *stream, int32_t sliding_window);
+
+/*
+ * pa_decode_multi - paged attention of q_len new tokens per sequence (several
+ * speculative tokens checked in one pass, "LLM推理引擎深度实战：…", §6.1; a chunk of a
+ * long prompt, "大模型推理引擎优化：…", §4.1), causal within the new chunk.
+ *
+ * query and out are [num_seqs, q_len, num_heads, head_dim] (q_dtype);
+ * context_lens count the q_len new tokens, which must already be in the cache
+ * (pa_append_kv with num_seqs * q_len slots).  New token i of sequence b sits at
+ * position L - q_len + i and attends to tokens 0 .. L - q_len + i (a zero row
+ * when that range is empty).  q_len 1..4096; every other argument is as for
+ * pa_decode, with the workspace size from pa_decode_multi_workspace_bytes.
+ * Rows of (query, head) fill 16-row matrix-core tiles: a tile holds the heads of
+ * one KV head and as many of a sequence's queries as fit.
+ */
+pa_status pa_decode_multi(void *out, const void *query,
+                          const void *key_cache, const void *value_cache,
+                          const float *k_scale, const float *v_scale,
+                          const int32_t *block_tables, const int32_t *context_lens,
+                          int32_t num_seqs, int32_t q_len, int32_t num_heads,
+                          int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                          int32_t max_blocks_per_seq, int32_t max_context_len,
+                          float scale, int32_t partition_size,
+                          int32_t q_dtype, int32_t cache_dtype,
+                          void *workspace, size_t workspace_bytes,
+                          void *stream);
+
+/* pa_decode_multi_workspace_bytes - workspace pa_decode_multi needs ((size_t)-1: invalid). */
+size_t pa_decode_multi_workspace_bytes(int32_t num_seqs, int32_t q_len, int32_t num_heads,
+                                       int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t max_context_len, int32_t partition_size);
 
 /* pa_status_string - static, human-readable name of a status code. */
 const char *pa_status_string(int32_t status);

@@ -18,6 +18,7 @@ from .binding import (  # noqa: F401
     pa_append_kv,
     pa_copy_blocks,
     pa_decode,
+    pa_decode_multi,
     pa_decode_sliding,
     pa_swap_blocks,
 )

@@ -57,6 +57,11 @@ def load_library(path=LIB_PATH):
     lib.pa_decode.restype = i32
     lib.pa_decode_sliding.argtypes = lib.pa_decode.argtypes + [i32]
     lib.pa_decode_sliding.restype = i32
+    lib.pa_decode_multi.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i64, i32, i32,
+                                    ctypes.c_float, i32, i32, i32, vp, sz, vp]
+    lib.pa_decode_multi.restype = i32
+    lib.pa_decode_multi_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    lib.pa_decode_multi_workspace_bytes.restype = sz
     lib.pa_status_string.argtypes = [i32]
     lib.pa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -215,4 +220,33 @@ def _decode(window, out, query, key_cache, value_cache, block_tables, context_le
             _DTYPE[key_cache.dtype], _ptr(workspace), ws_bytes, _stream(stream)]
     lib = load_library()
     _check(lib.pa_decode(*args) if window is None else lib.pa_decode_sliding(*args, window))
+    return out
+
+
+def pa_decode_multi(out, query, key_cache, value_cache, block_tables, context_lens, scale, max_context_len,
+                    partition_size=0, k_scale=None, v_scale=None, workspace=None, stream=None):
+    """Attention of query[B, Q, Hq, D] (Q new tokens per sequence, causal within them) -> out[B, Q, Hq, D].
+
+    context_lens count the Q new tokens, already appended to the cache.
+    """
+    _on_gpu(out, query, key_cache, value_cache, block_tables, context_lens, k_scale, v_scale, workspace)
+    B, q_len, hq, d = query.shape
+    nb, bs, hkv, dk = key_cache.shape
+    if out.shape != query.shape or out.dtype != query.dtype or bs != BLOCK_SIZE or dk != d or \
+            value_cache.shape != key_cache.shape or block_tables.dim() != 2 or \
+            block_tables.shape[0] != B or context_lens.shape != (B,) or \
+            block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("inconsistent shapes for pa_decode_multi")
+    lib = load_library()
+    if workspace is None:
+        n = lib.pa_decode_multi_workspace_bytes(B, q_len, hq, hkv, d, int(max_context_len), int(partition_size))
+        if n == ctypes.c_size_t(-1).value:
+            raise PagedAttnError(2, "invalid arguments for pa_decode_multi_workspace_bytes")
+        workspace = torch.empty(n, dtype=torch.uint8, device=query.device) if n else None
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.pa_decode_multi(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(k_scale), _ptr(v_scale),
+        _ptr(block_tables), _ptr(context_lens), B, q_len, hq, hkv, d, nb, block_tables.shape[1],
+        int(max_context_len), float(scale), int(partition_size), _DTYPE[query.dtype], _DTYPE[key_cache.dtype],
+        _ptr(workspace), ws_bytes, _stream(stream)))
     return out

@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <algorithm>
 #include <cstdint>
 
 #include "pa_internal.h"
@@ -16,6 +17,7 @@ namespace {
 constexpr int32_t kMaxPartition = 1 << 20;
 constexpr int64_t kMaxWork = ((int64_t)1 << 30);  // waves, or (head group, block) pairs, per launch
 constexpr int64_t kBalancedWaves = 2048;            // waves of the balanced split (8 per CU)
+constexpr int32_t kMaxQueries = 4096;               // new tokens per sequence in one multi-query call
 
 // Launch shape shared by pa_decode and pa_decode_workspace_bytes.
 struct Plan {
@@ -24,6 +26,8 @@ struct Plan {
     int64_t part;        // fixed split: partition tokens
     int64_t np;          // fixed split: partitions per sequence
     int64_t hpw;         // heads per wave
+    int64_t qpw;         // queries per wave (rows = qpw x hpw)
+    int64_t qgroups;     // query groups per head group
     bool mfma;           // matrix-core path
     int64_t groups;      // head groups per sequence
     int64_t waves;       // waves in the grid
@@ -31,16 +35,19 @@ struct Plan {
 };
 
 Plan make_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
-               int32_t max_context_len, int32_t partition_size) {
+               int32_t max_context_len, int32_t partition_size, int32_t q_len = 1) {
     Plan pl{};
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 || head_dim <= 0 ||
         max_context_len < 0 || partition_size < 0 || partition_size % PA_BLOCK_SIZE != 0 ||
-        partition_size > kMaxPartition)
+        partition_size > kMaxPartition || q_len < 1 || q_len > kMaxQueries)
         return pl;
-    const pa::HeadGrouping hg = pa::head_grouping(num_heads / num_kv_heads);
+    const pa::HeadGrouping hg = q_len == 1 ? pa::head_grouping(num_heads / num_kv_heads)
+                                           : pa::multi_query_grouping(num_heads / num_kv_heads);
     pl.hpw = hg.hpw;
     pl.mfma = hg.mfma;
-    pl.groups = num_heads / pl.hpw;
+    pl.qpw = q_len == 1 ? 1 : std::min<int64_t>(q_len, 16 / pl.hpw);
+    pl.qgroups = (q_len + pl.qpw - 1) / pl.qpw;
+    pl.groups = num_heads / pl.hpw * pl.qgroups;
     const int64_t seq_groups = (int64_t)num_seqs * pl.groups;
     const int64_t max_blocks = (max_context_len + PA_BLOCK_SIZE - 1) / PA_BLOCK_SIZE;
     if (seq_groups * (max_blocks > 0 ? max_blocks : 1) >= kMaxWork) return pl;
@@ -62,7 +69,7 @@ Plan make_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_
 }
 
 size_t workspace_size(const Plan& pl, int32_t head_dim) {
-    return (size_t)pl.slots * (size_t)pl.hpw * (size_t)(head_dim + 2) * sizeof(float);
+    return (size_t)pl.slots * (size_t)(pl.hpw * pl.qpw) * (size_t)(head_dim + 2) * sizeof(float);
 }
 
 bool aligned(const void* ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) == 0; }
@@ -116,7 +123,7 @@ pa_status decode_impl(void* out, const void* query, const void* key_cache, const
                     const int32_t* context_lens, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                     int32_t head_dim, int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
                     float scale, int32_t partition_size, int32_t q_dtype, int32_t cache_dtype, void* workspace,
-                    size_t workspace_bytes, void* stream, int32_t window) {
+                    size_t workspace_bytes, void* stream, int32_t window, int32_t q_len) {
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 ||
         num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || num_heads > 65536)
         return PA_ERR_SHAPE;
@@ -125,7 +132,7 @@ pa_status decode_impl(void* out, const void* query, const void* key_cache, const
     const bool fp8 = cache_dtype == PA_FP8_E4M3;
     if (!fp8 && cache_dtype != q_dtype) return PA_ERR_DTYPE;
     if (!std::isfinite(scale) || window < 0) return PA_ERR_SHAPE;
-    const Plan pl = make_plan(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, partition_size);
+    const Plan pl = make_plan(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, partition_size, q_len);
     if (!pl.ok) return PA_ERR_SHAPE;
     const size_t need = workspace_size(pl, head_dim);
     if (num_seqs == 0) return PA_OK;
@@ -148,7 +155,7 @@ pa_status decode_impl(void* out, const void* query, const void* key_cache, const
     p.context_lens = context_lens;
     if (need > 0) {
         p.ws_acc = (float*)workspace;
-        p.ws_ml = p.ws_acc + (size_t)pl.slots * pl.hpw * head_dim;
+        p.ws_ml = p.ws_acc + (size_t)pl.slots * pl.hpw * pl.qpw * head_dim;
     }
     p.num_blocks = num_blocks;
     p.B = num_seqs;
@@ -162,6 +169,10 @@ pa_status decode_impl(void* out, const void* query, const void* key_cache, const
     p.part_blocks = (int32_t)(pl.part / PA_BLOCK_SIZE);
     p.groups = (int32_t)pl.groups;
     p.hpw = (int32_t)pl.hpw;
+    p.qlen = q_len;
+    p.qpw = (int32_t)pl.qpw;
+    p.qgroups = (int32_t)pl.qgroups;
+    p.rows = (int32_t)(pl.qpw * pl.hpw);
     p.mfma = pl.mfma ? 1 : 0;
     p.num_waves = (int32_t)pl.waves;
     p.window = window;
@@ -275,7 +286,7 @@ pa_status pa_decode(void* out, const void* query, const void* key_cache, const v
                     size_t workspace_bytes, void* stream) {
     return decode_impl(out, query, key_cache, value_cache, k_scale, v_scale, block_tables, context_lens, num_seqs,
                        num_heads, num_kv_heads, head_dim, num_blocks, max_blocks_per_seq, max_context_len, scale,
-                       partition_size, q_dtype, cache_dtype, workspace, workspace_bytes, stream, 0);
+                       partition_size, q_dtype, cache_dtype, workspace, workspace_bytes, stream, 0, 1);
 }
 
 pa_status pa_decode_sliding(void* out, const void* query, const void* key_cache, const void* value_cache,
@@ -287,7 +298,27 @@ pa_status pa_decode_sliding(void* out, const void* query, const void* key_cache,
                             int32_t sliding_window) {
     return decode_impl(out, query, key_cache, value_cache, k_scale, v_scale, block_tables, context_lens, num_seqs,
                        num_heads, num_kv_heads, head_dim, num_blocks, max_blocks_per_seq, max_context_len, scale,
-                       partition_size, q_dtype, cache_dtype, workspace, workspace_bytes, stream, sliding_window);
+                       partition_size, q_dtype, cache_dtype, workspace, workspace_bytes, stream, sliding_window,
+                       1);
+}
+
+pa_status pa_decode_multi(void* out, const void* query, const void* key_cache, const void* value_cache,
+                          const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                          const int32_t* context_lens, int32_t num_seqs, int32_t q_len, int32_t num_heads,
+                          int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks, int32_t max_blocks_per_seq,
+                          int32_t max_context_len, float scale, int32_t partition_size, int32_t q_dtype,
+                          int32_t cache_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    if (q_len < 1 || q_len > kMaxQueries) return PA_ERR_SHAPE;
+    return decode_impl(out, query, key_cache, value_cache, k_scale, v_scale, block_tables, context_lens, num_seqs,
+                       num_heads, num_kv_heads, head_dim, num_blocks, max_blocks_per_seq, max_context_len, scale,
+                       partition_size, q_dtype, cache_dtype, workspace, workspace_bytes, stream, 0, q_len);
+}
+
+size_t pa_decode_multi_workspace_bytes(int32_t num_seqs, int32_t q_len, int32_t num_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t max_context_len, int32_t partition_size) {
+    const Plan pl = make_plan(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, partition_size, q_len);
+    if (!pl.ok) return (size_t)-1;
+    return workspace_size(pl, head_dim);
 }
 
 }  // extern "C"

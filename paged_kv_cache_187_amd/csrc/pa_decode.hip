@@ -531,13 +531,23 @@ struct MfmaSegment {
         }
     }
 
-    static __device__ __forceinline__ void run(const DecodeParams& p, int lane, int b, int hg, int jb, int je,
+    // Unit u of sequence b: head group u / qgroups (G = hpw heads of one KV head) and query
+    // group u % qgroups (qpw consecutive new tokens).  Row c < rows of the tile is query
+    // c / G of the group and head c % G; with one query per sequence the rows are the heads.
+    static __device__ __forceinline__ void run(const DecodeParams& p, int lane, int b, int u, int jb, int je,
                                                int jfirst, int nblk, int lo, int L, int64_t slot) {
         const int G = p.hpw;
+        const int hg = u / p.qgroups;
+        const int q0 = (u % p.qgroups) * p.qpw;        // first query of the unit
         const int h0 = hg * G;
         const int hk = h0 / (p.Hq / p.Hkv);
         const int c = lane & 15;
         const int g = lane >> 4;
+        // Row of this lane's softmax column: its query, and the last token that query sees
+        // (new token qi sits at position L - qlen + qi and attends to tokens up to there).
+        const int qi = q0 + c / G;
+        const bool row_ok = c < p.rows && qi < p.qlen;
+        const int last = L - p.qlen + qi;
 
         const int32_t* table = p.block_tables + (int64_t)b * p.max_blocks;
         auto table_chunk = [&](int jbase) {
@@ -546,13 +556,13 @@ struct MfmaSegment {
         };
         int tbl = table_chunk(jb);
 
-        // Q as the B operand: lane l holds Q[head c][dk(s, g) + i]; zero past the group.
+        // Q as the B operand: lane l holds Q[row c][dk(s, g) + i]; zero for rows past the unit.
         uint4 qb[KSTEPS];
         {
-            const bool hv = c < G;
-            const uint16_t* qrow = (const uint16_t*)p.query + ((int64_t)b * p.Hq + h0 + (hv ? c : 0)) * D;
+            const int64_t qrow_idx = ((int64_t)b * p.qlen + (row_ok ? qi : 0)) * p.Hq + h0 + (row_ok ? c % G : 0);
+            const uint16_t* qrow = (const uint16_t*)p.query + qrow_idx * D;
 #pragma unroll
-            for (int s = 0; s < KSTEPS; ++s) qb[s] = hv ? *(const uint4*)(qrow + dk(s, g)) : uint4{0u, 0u, 0u, 0u};
+            for (int s = 0; s < KSTEPS; ++s) qb[s] = row_ok ? *(const uint4*)(qrow + dk(s, g)) : uint4{0u, 0u, 0u, 0u};
         }
 
         f32x4_t O[E];
@@ -603,14 +613,17 @@ struct MfmaSegment {
             }
             const float ksc[4] = {bf.ks.x, bf.ks.y, bf.ks.z, bf.ks.w};
             const float vsc[4] = {bf.vs.x, bf.vs.y, bf.vs.z, bf.vs.w};
+            // valid: the token holds data this unit reads (V rows of other tokens select zeros);
+            // seen: this lane's row attends to it (its query's causal limit).
             float sc[4];
-            bool valid[4];
+            bool valid[4], seen[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = j * kBlockSize + 4 * g + r;
                 valid[r] = t >= lo && t < L;
+                seen[r] = valid[r] && t <= last;
                 const float f = kFp8 ? p.scale_log2 * ksc[r] : p.scale_log2;
-                sc[r] = valid[r] ? S[r] * f : kNegInf;
+                sc[r] = seen[r] ? S[r] * f : kNegInf;
             }
             float mb = __builtin_fmaxf(__builtin_fmaxf(sc[0], sc[1]), __builtin_fmaxf(sc[2], sc[3]));
             mb = __builtin_fmaxf(mb, __shfl_xor(mb, 16));
@@ -625,10 +638,10 @@ struct MfmaSegment {
             for (int r = 0; r < 4; ++r) {
                 pr[r] = fast_exp2(sc[r] - ms);
                 psum += pr[r];
-                if constexpr (kFp8) pr[r] = valid[r] ? pr[r] * vsc[r] : 0.0f;
+                if constexpr (kFp8) pr[r] = seen[r] ? pr[r] * vsc[r] : 0.0f;
             }
             lsum = lsum * alpha + psum;
-            // Rescale the output rows (heads 4g + r) when some running max moved.
+            // Rescale the output rows 4g + r when some running max moved.
             if (__ballot(alpha != 1.0f)) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -674,15 +687,18 @@ struct MfmaSegment {
 
         stream_blocks<NB, Buf>(jb, je, tbl, table_chunk, issue, consume);
 
-        // Totals per head (lane groups hold disjoint tokens), then per output row 4g + r.
+        // Totals per row (lane groups hold disjoint tokens), then per output row 4g + r.
         float ltot = lsum + __shfl_xor(lsum, 16);
         ltot += __shfl_xor(ltot, 32);
         const bool whole = jb == jfirst && je == nblk;
+        const int R = p.rows;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int head = 4 * g + r;
-            const float lr = __shfl(ltot, head);
-            if (head >= G) continue;
+            const int row = 4 * g + r;
+            const float lr = __shfl(ltot, row);
+            const int rq = q0 + row / G;               // query and head of this output row
+            if (row >= R || rq >= p.qlen) continue;
+            const int head = h0 + row % G;
             if (whole) {
                 const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
                 uint32_t packed[E / 2];
@@ -690,22 +706,22 @@ struct MfmaSegment {
                 for (int k = 0; k < E / 2; ++k)
                     packed[k] = (uint32_t)to_bits(QT{}, O[2 * k][r] * inv) |
                                 ((uint32_t)to_bits(QT{}, O[2 * k + 1][r] * inv) << 16);
-                uint16_t* orow = (uint16_t*)p.out + ((int64_t)b * p.Hq + h0 + head) * D + E * c;
+                uint16_t* orow = (uint16_t*)p.out + (((int64_t)b * p.qlen + rq) * p.Hq + head) * D + E * c;
                 if constexpr (E == 8) {
                     *(uint4*)orow = uint4{packed[0], packed[1], packed[2], packed[3]};
                 } else {
                     *(uint2*)orow = uint2{packed[0], packed[1]};
                 }
             } else {
-                float4* arow = (float4*)(p.ws_acc + (slot * G + head) * D + E * c);
+                float4* arow = (float4*)(p.ws_acc + (slot * R + row) * D + E * c);
 #pragma unroll
                 for (int q = 0; q < E / 4; ++q)
                     arow[q] = float4{O[4 * q][r], O[4 * q + 1][r], O[4 * q + 2][r], O[4 * q + 3][r]};
             }
         }
-        if (!whole && g == 0 && c < G) {
-            p.ws_ml[(slot * G + c) * 2] = m;
-            p.ws_ml[(slot * G + c) * 2 + 1] = ltot;
+        if (!whole && g == 0 && row_ok) {
+            p.ws_ml[(slot * R + c) * 2] = m;
+            p.ws_ml[(slot * R + c) * 2 + 1] = ltot;
         }
     }
 };
@@ -769,9 +785,9 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
-// Merge of the partials of one (sequence, query head), one wave each:
+// Merge of the partials of one output row (sequence, query, head), one wave each:
 // out = sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k over the segments of its
-// head group in ascending token order (M = max_k m_k).  Lane k reads the (m, l)
+// unit in ascending token order (M = max_k m_k).  Lane k reads the (m, l)
 // pair of partial k, so all pairs arrive in one round; the V sums are then
 // folded in order k = 0, 1, ... with every lane holding D/64 columns.  Also
 // writes the zero rows of empty sequences in the balanced split (no segment
@@ -781,12 +797,14 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodePara
     constexpr int EPT = D / kWave;
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t row = (int64_t)blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    if (row >= (int64_t)p.B * p.Hq) return;
-    const int b = (int)(row / p.Hq);
-    const int h = (int)(row % p.Hq);
-    const int hg = h / p.hpw;
-    const int hh = h % p.hpw;
-    const int64_t s = (int64_t)b * p.groups + hg;
+    const int64_t per_seq = (int64_t)p.qlen * p.Hq;
+    if (row >= (int64_t)p.B * per_seq) return;
+    const int b = (int)(row / per_seq);
+    const int qi = (int)(row % per_seq) / p.Hq;       // query (new token) of the row
+    const int h = (int)(row % per_seq) % p.Hq;
+    const int u = (h / p.hpw) * p.qgroups + qi / p.qpw;   // unit of (head group, query group)
+    const int hh = (qi % p.qpw) * p.hpw + h % p.hpw;      // row within the unit's slots
+    const int64_t s = (int64_t)b * p.groups + u;
     uint16_t* orow = (uint16_t*)p.out + row * D;
 
     int64_t first;
@@ -806,7 +824,7 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodePara
             for (int k = 0; k < EPT; ++k) orow[k * kWave + lane] = to_bits(QT{}, 0.0f);
             return;
         }
-        const int pos0 = p.groups * e.start + hg * e.nblk;
+        const int pos0 = p.groups * e.start + u * e.nblk;
         const int t0 = rg.range_of(pos0);
         const int t1 = rg.range_of(pos0 + e.nblk - 1);
         if (t0 == t1) return;               // one segment: written directly
@@ -814,7 +832,7 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodePara
         count = t1 - t0 + 1;
     }
 
-    const int hpw = p.hpw;
+    const int hpw = p.rows;                 // partial rows per slot
     const float* ml = p.ws_ml;
     const float* acc = p.ws_acc + (first * hpw + hh) * D + lane;   // partial k at acc[k * hpw * D]
     const int64_t kstride = (int64_t)hpw * D;
@@ -890,7 +908,7 @@ hipError_t run(const DecodeParams& p, hipStream_t stream) {
     const int64_t grid = ((int64_t)p.num_waves + kWaves - 1) / kWaves;
     hipLaunchKernelGGL((decode_kernel<Segment>), dim3((uint32_t)grid), dim3(kThreads), 0, stream, p);
     if (p.balanced || p.NP > 1) {
-        const int64_t rows = (int64_t)p.B * p.Hq;   // one merge wave per (sequence, query head)
+        const int64_t rows = (int64_t)p.B * p.qlen * p.Hq;   // one merge wave per (sequence, query, head)
         hipLaunchKernelGGL((decode_merge_kernel<QT, D>), dim3((uint32_t)((rows + kWaves - 1) / kWaves)),
                            dim3(kThreads), 0, stream, p);
     }
@@ -931,6 +949,16 @@ HeadGrouping head_grouping(int group) {
     for (int h = 8; h > 1; h >>= 1)
         if (group % h == 0) return {h, false};
     return {1, false};
+}
+
+HeadGrouping multi_query_grouping(int group) {
+    // Several queries per sequence always take the matrix cores: a unit holds the heads of
+    // one KV head (up to 16; larger groups split into the largest divisor <= 16) and as
+    // many of the sequence's queries as fill the 16 rows.
+    if (group <= 16) return {group, true};
+    for (int h = 16; h > 1; --h)
+        if (group % h == 0) return {h, true};
+    return {1, true};
 }
 
 hipError_t launch_decode(const DecodeParams& p, int head_dim, int q_kind, int cache_kind, hipStream_t stream) {

@@ -26,7 +26,11 @@ struct DecodeParams {
     int32_t balanced;          // 1: equal (sequence, head group, block) ranges per wave
     int32_t NP;                // fixed split: partitions per sequence in the grid
     int32_t part_blocks;       // fixed split: partition length in 16-token blocks
-    int32_t groups;            // head groups per sequence = Hq / hpw
+    int32_t groups;            // work units per sequence = (Hq / hpw) head groups x qgroups query groups
+    int32_t qlen;              // new tokens (queries) per sequence: 1 for decode
+    int32_t qpw;               // queries per unit (matrix-core path): rows = qpw x hpw <= 16
+    int32_t qgroups;           // query groups per head group = ceil(qlen / qpw)
+    int32_t rows;              // rows per unit = qpw x hpw (partial-result rows per slot)
     int32_t hpw;               // query heads per wave (all share one KV head)
     int32_t mfma;              // 1: matrix-core path (hpw <= 16 rows of a 16x16 tile)
     int32_t num_waves;         // waves in the grid
@@ -57,7 +61,8 @@ struct HeadGrouping {
     int hpw;
     bool mfma;
 };
-HeadGrouping head_grouping(int group);
+HeadGrouping head_grouping(int group);          // one query per sequence
+HeadGrouping multi_query_grouping(int group);  // several queries per sequence
 
 hipError_t launch_decode(const DecodeParams& p, int head_dim, int q_kind, int cache_kind, hipStream_t stream);
 

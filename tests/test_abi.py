@@ -35,9 +35,9 @@ def lib():
 
 
 def test_header_declares_the_boundary():
-    assert _declared() == ["pa_append_kv", "pa_copy_blocks", "pa_decode", "pa_decode_partition_size",
-                           "pa_decode_sliding", "pa_decode_workspace_bytes", "pa_status_string",
-                           "pa_swap_blocks"]
+    assert _declared() == ["pa_append_kv", "pa_copy_blocks", "pa_decode", "pa_decode_multi",
+                           "pa_decode_multi_workspace_bytes", "pa_decode_partition_size", "pa_decode_sliding",
+                           "pa_decode_workspace_bytes", "pa_status_string", "pa_swap_blocks"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -80,6 +80,20 @@ def _decode(lib, **kw):
     return lib.pa_decode(a["out"], a["query"], a["key_cache"], a["value_cache"], a["k_scale"], a["v_scale"],
                          a["block_tables"], a["context_lens"], a["B"], a["Hq"], a["Hkv"], a["D"], a["nb"],
                          a["mb"], a["maxL"], a["scale"], a["part"], a["qd"], a["cd"], a["ws"], a["wsb"], None)
+
+
+def test_multi_query_workspace_and_checks(lib):
+    # MHA, 4 queries: one unit per head (4 of 16 rows), slots = waves + (seq, unit) pairs
+    assert lib.pa_decode_multi_workspace_bytes(2, 4, 4, 4, 64, 20, 0) == (16 + 8) * 4 * 66 * 4
+    # GQA group 8 with 3 queries: 2 queries per 16-row unit -> 2 query groups per KV head
+    assert lib.pa_decode_multi_workspace_bytes(1, 3, 8, 1, 128, 16, 0) == (2 + 2) * 16 * 130 * 4
+    assert lib.pa_decode_multi_workspace_bytes(1, 0, 8, 1, 128, 16, 0) == ctypes.c_size_t(-1).value
+    st = lib.pa_decode_multi(FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, 2, 0, 8, 2, 128, 10, 4, 64, 0.1, 0,
+                             F16, F16, None, 0, None)
+    assert st == SHAPE                                       # q_len 0
+    st = lib.pa_decode_multi(FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, 0, 4, 8, 2, 128, 10, 4, 64, 0.1, 0,
+                             F16, F16, None, 0, None)
+    assert st == OK                                          # no sequences
 
 
 def test_sliding_decode_host_checks(lib):
