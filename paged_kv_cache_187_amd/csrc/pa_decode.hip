@@ -297,9 +297,9 @@ static __device__ __forceinline__ void run(const DecodeParams& p, int lane, int 
         const char* kb = kbase + pb * blk_bytes;
         const char* vb = vbase + pb * blk_bytes;
 #pragma unroll
-        for (int i = 0; i < LPB; ++i) kr[i] = *(const uint4*)(kb + lane_off + i * load_step);
+        for (int i = 0; i < LPB; ++i) kr[i] = load_stream((const uint4*)(kb + lane_off + i * load_step));
 #pragma unroll
-        for (int i = 0; i < LPB; ++i) vr[i] = *(const uint4*)(vb + lane_off + i * load_step);
+        for (int i = 0; i < LPB; ++i) vr[i] = load_stream((const uint4*)(vb + lane_off + i * load_step));
         if constexpr (kFp8) {
 #pragma unroll
             for (int i = 0; i < LPB; ++i) {
@@ -587,10 +587,12 @@ struct MfmaSegment {
             const char* vb = vbase + pb * blk_bytes;
             // K: lane l reads 16 bytes of token c (16-bit: step s at byte 64 s + 16 g;
             // FP8: steps 2i, 2i+1 at byte 64 i + 16 g).  V: rows 4g + i, E elements at E c.
+            // K lines are read in two halves by two of these loads (and shared-prefix blocks by
+            // several sequences), so K stays cacheable; V rows are read once, in full lines.
 #pragma unroll
             for (int i = 0; i < KLOADS; ++i) bf.k[i] = *(const uint4*)(kb + k_off + 64 * i);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) bf.v[i] = *(const VT*)(vb + v_off + i * v_step);
+            for (int i = 0; i < 4; ++i) bf.v[i] = load_stream((const VT*)(vb + v_off + i * v_step));
             if constexpr (kFp8) {
                 bf.ks = *(const float4*)(p.k_scale + pb * kBlockSize + 4 * g);
                 bf.vs = *(const float4*)(p.v_scale + pb * kBlockSize + 4 * g);
