@@ -50,16 +50,18 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(const CopyPoo
     const uint4* from = (is_v ? c.src_v : c.src_k) + src * block_vecs;
     uint4* to = (is_v ? c.dst_v : c.dst_k) + dst * block_vecs;
     const int64_t base = (int64_t)blockIdx.z * kChunkVecs + threadIdx.x;
+    // Each byte is moved once: streaming (non-temporal) loads and stores keep the copy from
+    // displacing cached data of concurrent work.
     uint4 v[kCopyVecs];
 #pragma unroll
     for (int i = 0; i < kCopyVecs; ++i) {
         const int64_t k = base + (int64_t)i * kCopyThreads;
-        if (k < block_vecs) v[i] = from[k];
+        if (k < block_vecs) v[i] = load_stream(from + k);
     }
 #pragma unroll
     for (int i = 0; i < kCopyVecs; ++i) {
         const int64_t k = base + (int64_t)i * kCopyThreads;
-        if (k < block_vecs) to[k] = v[i];
+        if (k < block_vecs) store_stream(to + k, v[i]);
     }
     const float* sfrom = is_v ? c.src_vs : c.src_ks;
     float* sto = is_v ? c.dst_vs : c.dst_ks;

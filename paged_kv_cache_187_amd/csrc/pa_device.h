@@ -41,6 +41,9 @@ __device__ __forceinline__ uint2 load_stream(const uint2* p) {
     return __builtin_bit_cast(uint2, __builtin_nontemporal_load((const u32x2_t*)p));
 }
 __device__ __forceinline__ uint32_t load_stream(const uint32_t* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void store_stream(uint4* p, uint4 v) {
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, v), (u32x4_t*)p);
+}
 
 // ---------------------------------------------------------------------------
 // Conversions of packed 32-bit words to float32 (all exact).
