@@ -185,9 +185,11 @@ __device__ Ranges make_ranges(const DecodeParams& p, int T) {
 // Streams logical blocks [jb, je) of one sequence through NB register buffers:
 // consume(j, buf) runs for every block in order while the loads of the next NB-1
 // blocks are in flight.  Every issue is unconditional (the compiler can then count
-// the loads and wait exactly for the oldest buffer); issues past the end re-read
-// the last block, which is still in L2, and are never consumed.  The page table is
-// read 64 ids at a time, one per lane (`tbl`, refreshed by table_chunk).
+// the loads and wait exactly for the oldest buffer): an issue for a block past the end
+// of the current 64-block chunk loads through an empty buffer descriptor, which
+// returns zeros without touching memory, and is never consumed.  The page table is
+// read 64 ids at a time, one per lane (`tbl`, refreshed by table_chunk);
+// issue(j, jend, jbase, buf) gets the chunk's end so it can tell live blocks apart.
 template <int NB, typename Buf, typename TableFn, typename IssueFn, typename ConsumeFn>
 __device__ __forceinline__ void stream_blocks(int jb, int je, int& tbl, TableFn table_chunk, IssueFn issue,
                                               ConsumeFn consume) {
@@ -196,18 +198,24 @@ __device__ __forceinline__ void stream_blocks(int jb, int je, int& tbl, TableFn 
     for (int jc = jb; jc < je; jc += kWave) {
         if (jc != jb) tbl = table_chunk(jc);
         const int jend = min(je, jc + kWave);
-        const int last = jend - 1;
 #pragma unroll
-        for (int k = 0; k < NB - 1; ++k) ok[k] = issue(min(jc + k, last), jc, buf[k]);
+        for (int k = 0; k < NB - 1; ++k) ok[k] = issue(jc + k, jend, jc, buf[k]);
         for (int j = jc; j < jend; j += NB) {
 #pragma unroll
             for (int k = 0; k < NB; ++k) {
                 const int nk = (k + NB - 1) % NB;
-                ok[nk] = issue(min(j + k + NB - 1, last), jc, buf[nk]);
+                ok[nk] = issue(j + k + NB - 1, jend, jc, buf[nk]);
                 if (j + k < jend && ok[k]) consume(j + k, buf[k]);
             }
         }
     }
+}
+
+// Physical block of logical block j (< jend) from the chunk held in `tbl`; -1 when j is
+// past the end or the table entry is outside the pool.
+__device__ __forceinline__ int live_block(const DecodeParams& p, int tbl, int j, int jend, int jbase) {
+    const int phys = __builtin_amdgcn_readlane(tbl, (j < jend ? j : jend - 1) - jbase);
+    return (j < jend && phys >= 0 && phys < p.num_blocks) ? phys : -1;
 }
 
 // VALU path (head groups of 1, 2, 4 or 8 query heads).  One segment: blocks [jb, je) of
@@ -282,24 +290,24 @@ static __device__ __forceinline__ void run(const DecodeParams& p, int lane, int 
     const char* vbase = (const char*)p.value_cache;
 
     // Issue the loads of logical block j (K, V and, for FP8, the per-token scales), whose
-    // physical id is lane j - jbase of `tbl`.  The loads are unconditional so that the
-    // compiler can count them exactly (the consumer of the older buffer then waits only for
-    // its own loads); an out-of-range physical id reads block 0 instead and the function
-    // returns false so that the block is skipped.
-    auto issue = [&](int j, int jbase, Buf& bf) {
+    // physical id is lane j - jbase of `tbl`.  The K/V loads go through a descriptor of
+    // the block (streaming: read once); past the chunk's end or for an id outside the pool
+    // the descriptor is empty (zeros, no memory traffic) and the function returns false so
+    // that the block is skipped.
+    auto issue = [&](int j, int jend, int jbase, Buf& bf) {
         uint4(&kr)[LPB] = bf.k;
         uint4(&vr)[LPB] = bf.v;
         float(&ksc)[LPB] = bf.ks;
         float(&vsc)[LPB] = bf.vs;
-        const int phys = __builtin_amdgcn_readlane(tbl, j - jbase);
-        const bool ok = phys >= 0 && phys < p.num_blocks;
+        const int phys = live_block(p, tbl, j, jend, jbase);
+        const bool ok = phys >= 0;
         const int64_t pb = ok ? phys : 0;
-        const char* kb = kbase + pb * blk_bytes;
-        const char* vb = vbase + pb * blk_bytes;
+        const auto rk = block_rsrc(kbase + pb * blk_bytes, ok ? (int)blk_bytes : 0);
+        const auto rv = block_rsrc(vbase + pb * blk_bytes, ok ? (int)blk_bytes : 0);
 #pragma unroll
-        for (int i = 0; i < LPB; ++i) kr[i] = load_stream((const uint4*)(kb + lane_off + i * load_step));
+        for (int i = 0; i < LPB; ++i) kr[i] = buffer_load16<kCacheStream>(rk, lane_off + i * load_step);
 #pragma unroll
-        for (int i = 0; i < LPB; ++i) vr[i] = load_stream((const uint4*)(vb + lane_off + i * load_step));
+        for (int i = 0; i < LPB; ++i) vr[i] = buffer_load16<kCacheStream>(rv, lane_off + i * load_step);
         if constexpr (kFp8) {
 #pragma unroll
             for (int i = 0; i < LPB; ++i) {
@@ -534,6 +542,13 @@ struct MfmaSegment {
     // Unit u of sequence b: head group u / qgroups (G = hpw heads of one KV head) and query
     // group u % qgroups (qpw consecutive new tokens).  Row c < rows of the tile is query
     // c / G of the group and head c % G; with one query per sequence the rows are the heads.
+    // One lane's V row piece (streaming load of VBYTES bytes).
+    static __device__ __forceinline__ VT load_v(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+        if constexpr (VBYTES == 16) return buffer_load16<kCacheStream>(r, off);
+        else if constexpr (VBYTES == 8) return buffer_load8<kCacheStream>(r, off);
+        else return buffer_load4<kCacheStream>(r, off);
+    }
+
     static __device__ __forceinline__ void run(const DecodeParams& p, int lane, int b, int u, int jb, int je,
                                                int jfirst, int nblk, int lo, int L, int64_t slot) {
         const int G = p.hpw;
@@ -579,20 +594,20 @@ struct MfmaSegment {
         const char* kbase = (const char*)p.key_cache;
         const char* vbase = (const char*)p.value_cache;
 
-        auto issue = [&](int j, int jbase, Buf& bf) {
-            const int phys = __builtin_amdgcn_readlane(tbl, j - jbase);
-            const bool ok = phys >= 0 && phys < p.num_blocks;
+        auto issue = [&](int j, int jend, int jbase, Buf& bf) {
+            const int phys = live_block(p, tbl, j, jend, jbase);
+            const bool ok = phys >= 0;
             const int64_t pb = ok ? phys : 0;
-            const char* kb = kbase + pb * blk_bytes;
-            const char* vb = vbase + pb * blk_bytes;
+            const auto rk = block_rsrc(kbase + pb * blk_bytes, ok ? (int)blk_bytes : 0);
+            const auto rv = block_rsrc(vbase + pb * blk_bytes, ok ? (int)blk_bytes : 0);
             // K: lane l reads 16 bytes of token c (16-bit: step s at byte 64 s + 16 g;
             // FP8: steps 2i, 2i+1 at byte 64 i + 16 g).  V: rows 4g + i, E elements at E c.
-            // K lines are read in two halves by two of these loads (and shared-prefix blocks by
-            // several sequences), so K stays cacheable; V rows are read once, in full lines.
+            // K lines are read in two halves by two of these loads (and shared-prefix blocks
+            // by several sequences), so K stays cacheable; V rows are read once, in full lines.
 #pragma unroll
-            for (int i = 0; i < KLOADS; ++i) bf.k[i] = *(const uint4*)(kb + k_off + 64 * i);
+            for (int i = 0; i < KLOADS; ++i) bf.k[i] = buffer_load16<kCacheNormal>(rk, k_off + 64 * i);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) bf.v[i] = load_stream((const VT*)(vb + v_off + i * v_step));
+            for (int i = 0; i < 4; ++i) bf.v[i] = load_v(rv, v_off + i * v_step);
             if constexpr (kFp8) {
                 bf.ks = *(const float4*)(p.k_scale + pb * kBlockSize + 4 * g);
                 bf.vs = *(const float4*)(p.v_scale + pb * kBlockSize + 4 * g);

@@ -41,6 +41,30 @@ __device__ __forceinline__ uint2 load_stream(const uint2* p) {
     return __builtin_bit_cast(uint2, __builtin_nontemporal_load((const u32x2_t*)p));
 }
 __device__ __forceinline__ uint32_t load_stream(const uint32_t* p) { return __builtin_nontemporal_load(p); }
+// Loads through a buffer descriptor that covers `bytes` bytes from `base`: lanes whose
+// offset falls outside the range read zeros without touching memory (a descriptor of 0
+// bytes turns a load into a no-op that still counts as an issued load).  kStream marks
+// the loads non-temporal.
+constexpr int kBufferConfig = 0x00020000;   // raw (untyped) buffer access on gfx9
+constexpr int kCacheNormal = 0;
+constexpr int kCacheStream = 2;             // nt: read once, evict first
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kBufferConfig);
+}
+template <int POLICY>
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, POLICY));
+}
+template <int POLICY>
+__device__ __forceinline__ uint2 buffer_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, POLICY));
+}
+template <int POLICY>
+__device__ __forceinline__ uint32_t buffer_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, POLICY);
+}
+
 __device__ __forceinline__ void store_stream(uint4* p, uint4 v) {
     __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, v), (u32x4_t*)p);
 }
