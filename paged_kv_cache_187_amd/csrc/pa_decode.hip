@@ -464,7 +464,9 @@ static __device__ __forceinline__ void run(const DecodeParams& p, int lane, int 
 // a 16x16 tile; unused rows carry zero queries).  Per 16-token block, with lane l in
 // row group g = l/16 and column c = l%16:
 //   S^T[token][head] = K[token][:] . Q[head][:]   16x16x32 MFMAs over the head dim, K as
-//       the A operand straight from HBM (lane l: token c), Q the B operand.
+//       the A operand (lane l: token c), Q the B operand.  K is loaded in whole rows and
+//       rearranged through a small per-wave LDS tile: loads that each cover a few full
+//       rows stream faster than loads that each take a slice of all 16 rows.
 //   online softmax per head on S^T (lane l: tokens 4g..4g+3 of head c), which is also the
 //       A-operand layout of P in the next product.
 //   O[head][col] += P[head][token] . V[token][col]   16x16x16 MFMAs, one per tile t < D/16;
@@ -502,6 +504,10 @@ struct MfmaSegment {
     static constexpr int E = D / 16;               // head-dim elements per lane per V row = tiles
     static constexpr int KLOADS = kFp8 ? KSTEPS / 2 : KSTEPS;   // 16-byte K loads per lane per block
     static constexpr int VBYTES = E * EB;          // V bytes per lane per row: 4, 8 or 16
+    static constexpr int KLPR = D * EB / 16;       // lanes per K row in a whole-row load
+    static constexpr int KTPL = kWave / KLPR;      // K rows per whole-row load
+    static constexpr int KRS = D * EB + 16;        // LDS row stride (padded against bank conflicts)
+    static_assert(KTPL * KLOADS == kBlockSize, "whole-row K loads cover the block");
     using VT = typename Bytes<VBYTES>::T;
 
     struct Buf {
@@ -588,11 +594,17 @@ struct MfmaSegment {
 
         const int64_t tok_bytes = (int64_t)p.Hkv * D * EB;
         const int64_t blk_bytes = tok_bytes * kBlockSize;
-        const uint32_t k_off = (uint32_t)(c * tok_bytes + (int64_t)hk * D * EB) + 16 * g;
         const uint32_t v_off = (uint32_t)(4 * g * tok_bytes + (int64_t)hk * D * EB) + VBYTES * c;
         const uint32_t v_step = (uint32_t)tok_bytes;
         const char* kbase = (const char*)p.key_cache;
         const char* vbase = (const char*)p.value_cache;
+        // K arrives in whole rows (lane l: 16 bytes at 16 (l % KLPR) of row KTPL i + l / KLPR)
+        // and is turned into the operand layout through this wave's LDS tile.
+        const uint32_t kr_off = (uint32_t)((lane / KLPR) * tok_bytes + (int64_t)hk * D * EB) + 16 * (lane % KLPR);
+        __shared__ uint4 ktiles[kWaves][kBlockSize * KRS / 16];
+        char* ktile = (char*)ktiles[__builtin_amdgcn_readfirstlane(threadIdx.x / kWave)];
+        char* kput = ktile + (lane / KLPR) * KRS + 16 * (lane % KLPR);
+        const char* kget = ktile + c * KRS + 16 * g;
 
         auto issue = [&](int j, int jend, int jbase, Buf& bf) {
             const int phys = live_block(p, tbl, j, jend, jbase);
@@ -600,12 +612,10 @@ struct MfmaSegment {
             const int64_t pb = ok ? phys : 0;
             const auto rk = block_rsrc(kbase + pb * blk_bytes, ok ? (int)blk_bytes : 0);
             const auto rv = block_rsrc(vbase + pb * blk_bytes, ok ? (int)blk_bytes : 0);
-            // K: lane l reads 16 bytes of token c (16-bit: step s at byte 64 s + 16 g;
-            // FP8: steps 2i, 2i+1 at byte 64 i + 16 g).  V: rows 4g + i, E elements at E c.
-            // K lines are read in two halves by two of these loads (and shared-prefix blocks
-            // by several sequences), so K stays cacheable; V rows are read once, in full lines.
+            // K: KTPL whole rows per load.  V: rows 4g + i, E elements at E c.  Both are read
+            // once, in full lines, and streamed past the caches.
 #pragma unroll
-            for (int i = 0; i < KLOADS; ++i) bf.k[i] = buffer_load16<kCacheNormal>(rk, k_off + 64 * i);
+            for (int i = 0; i < KLOADS; ++i) bf.k[i] = buffer_load16<kCacheStream>(rk, kr_off + (uint32_t)(i * KTPL * tok_bytes));
 #pragma unroll
             for (int i = 0; i < 4; ++i) bf.v[i] = load_v(rv, v_off + i * v_step);
             if constexpr (kFp8) {
@@ -616,16 +626,31 @@ struct MfmaSegment {
         };
 
         auto consume = [&](int j, const Buf& bf) {
+            // K rows -> LDS -> A operand (lane l: 16 bytes of token c at byte 64 i + 16 g, i.e.
+            // 16-bit step s = i, or FP8 steps 2i and 2i + 1).  The tile belongs to this wave
+            // alone; the fences keep the compiler from moving these accesses past each other.
+            uint4 ka[KLOADS];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+            for (int i = 0; i < KLOADS; ++i) *(uint4*)(kput + i * KTPL * KRS) = bf.k[i];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+            for (int i = 0; i < KLOADS; ++i) ka[i] = *(const uint4*)(kget + 64 * i);
+
             // S^T for the block's 16 tokens x 16 head rows (lane l: tokens 4g + r of head c).
             f32x4_t S = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
             if constexpr (!kFp8) {
 #pragma unroll
-                for (int s = 0; s < KSTEPS; ++s) S = Mma<M>::k32(bf.k[s], qb[s], S);
+                for (int s = 0; s < KSTEPS; ++s) S = Mma<M>::k32(ka[s], qb[s], S);
             } else {
 #pragma unroll
                 for (int i = 0; i < KLOADS; ++i) {
-                    S = Mma<M>::k32(widen8(bf.k[i].x, bf.k[i].y), qb[2 * i], S);
-                    S = Mma<M>::k32(widen8(bf.k[i].z, bf.k[i].w), qb[2 * i + 1], S);
+                    S = Mma<M>::k32(widen8(ka[i].x, ka[i].y), qb[2 * i], S);
+                    S = Mma<M>::k32(widen8(ka[i].z, ka[i].w), qb[2 * i + 1], S);
                 }
             }
             const float ksc[4] = {bf.ks.x, bf.ks.y, bf.ks.z, bf.ks.w};
