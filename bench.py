@@ -380,6 +380,7 @@ def main():
         r = time_workload(name, args.steps, args.warmup, args.replicas, partition_size=args.partition_size,
                           use_graphs=args.graphs)
         also[name] = summarize(name, r)
+        also[name]["traffic"] = measured_traffic(name)
         del r
         torch.cuda.empty_cache()
 
