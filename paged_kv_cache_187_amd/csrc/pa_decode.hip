@@ -495,6 +495,27 @@ __device__ __forceinline__ void words_of<uint4>(const uint4& w, uint32_t* out) {
     out[0] = w.x; out[1] = w.y; out[2] = w.z; out[3] = w.w;
 }
 
+// Max and sum over the four 16-lane groups (lanes c, c + 16, c + 32, c + 48), every
+// lane getting the result: gfx950's row and half-wave swaps, which stay in the VALU
+// (a shuffle would make two round trips through the LDS crossbar).
+__device__ __forceinline__ float group_max(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float y = __builtin_fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+    return __builtin_fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float group_sum(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Slack of the matrix-core path's softmax reference (log2 units): exponentials up to
+// 2^8 keep full relative precision in the hi + lo split and cannot overflow the fp32
+// accumulators.
+constexpr float kSlack = 8.0f;
+
 template <typename QT, typename CT, int D, int NB>
 struct MfmaSegment {
     using M = QT;
@@ -667,10 +688,12 @@ struct MfmaSegment {
                 const float f = kFp8 ? p.scale_log2 * ksc[r] : p.scale_log2;
                 sc[r] = seen[r] ? S[r] * f : kNegInf;
             }
-            float mb = __builtin_fmaxf(__builtin_fmaxf(sc[0], sc[1]), __builtin_fmaxf(sc[2], sc[3]));
-            mb = __builtin_fmaxf(mb, __shfl_xor(mb, 16));
-            mb = __builtin_fmaxf(mb, __shfl_xor(mb, 32));
-            const float mn = __builtin_fmaxf(m, mb);
+            // Block maximum of head c over the four lane groups.  The reference m moves only
+            // when the block exceeds it by more than kSlack (or on the first scores), so the
+            // exponentials stay <= 2^kSlack and most blocks skip the output rescale; any
+            // reference gives the same softmax, this one keeps the arithmetic in range.
+            const float mb = group_max(__builtin_fmaxf(__builtin_fmaxf(sc[0], sc[1]), __builtin_fmaxf(sc[2], sc[3])));
+            const float mn = (mb > m + kSlack) ? mb : m;
             const float ms = (mn == kNegInf) ? 0.0f : mn;
             const float alpha = fast_exp2(m - ms);
             m = mn;
@@ -730,8 +753,7 @@ struct MfmaSegment {
         stream_blocks<NB, Buf>(jb, je, tbl, table_chunk, issue, consume);
 
         // Totals per row (lane groups hold disjoint tokens), then per output row 4g + r.
-        float ltot = lsum + __shfl_xor(lsum, 16);
-        ltot += __shfl_xor(ltot, 32);
+        const float ltot = group_sum(lsum);
         const bool whole = jb == jfirst && je == nblk;
         const int R = p.rows;
 #pragma unroll
