@@ -209,3 +209,58 @@ def test_balanced_split_reused_workspace_repeats_bitwise(hq, hkv):
     for o in outs[1:]:
         assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
     assert_close(outs[0], oracle_decode(wh, oracle_caches(wh)), "bf16", "tiles")
+
+
+def _climbing_keys(wh, span):
+    """Rewrite the cached keys and this step's key so that every head's score climbs along its
+    context by about ``span`` (natural-log units): K[t] = (t + 1) * step * d + 0.1 * K_random[t],
+    with d the unit mean direction of the KV head's query heads.  The running maximum then moves
+    at almost every block, which exercises the rescaling of both kernels and the wide range of
+    partial maxima that the merge has to fold."""
+    cfg = wh.cfg
+    B, Hq, Hkv, D = cfg.num_seqs, cfg.num_heads, cfg.num_kv_heads, cfg.head_dim
+    G = Hq // Hkv
+    q = wh.query.float().view(B, Hkv, G, D)
+    d = q.mean(2)
+    d = d / d.norm(dim=-1, keepdim=True)
+    c = (q * d[:, :, None, :]).sum(-1).mean(-1).clamp(min=0.5) * cfg.scale   # [B, Hkv] score per unit of K along d
+    fp8 = cfg.cache_dtype == "fp8_e4m3"
+    src = wh.fill_key.float() if fp8 else wh.key_cache.float().view(-1, Hkv, D)
+    rows = {int(s): i for i, s in enumerate(wh.fill_slots.tolist())} if fp8 else None
+    new_cached = src.clone()
+    new_key = wh.key_new.float().clone()
+    for b in range(B):
+        L = int(wh.lens_np[b])
+        if L == 0:
+            continue
+        step = span / (c[b] * L)                                              # [Hkv]
+        for t in range(L):
+            slot = int(wh.tables_np[b][t // 16]) * 16 + t % 16
+            k = (t + 1) * step[:, None] * d[b]
+            if t == L - 1:
+                new_key[b] = k + 0.1 * new_key[b]
+            else:
+                r = rows[slot] if fp8 else slot
+                new_cached[r] = k + 0.1 * src[r]
+    if fp8:
+        wh.fill_key = new_cached.to(wh.fill_key.dtype)
+    else:
+        wh.key_cache = new_cached.view_as(wh.key_cache).to(wh.key_cache.dtype)
+    wh.key_new = new_key.to(wh.key_new.dtype)
+
+
+@pytest.mark.parametrize("qd,cd,hq,hkv,D,part", [
+    ("bf16", "bf16", 8, 1, 128, 0), ("f16", "f16", 4, 1, 64, 0), ("f16", "f16", 2, 2, 128, 0),
+    ("bf16", "fp8_e4m3", 8, 2, 128, 0), ("bf16", "bf16", 8, 1, 128, 64), ("f16", "f16", 1, 1, 128, 48)])
+def test_scores_climbing_along_the_context(qd, cd, hq, hkv, D, part):
+    """Scores that climb by ~200 (natural log) over the context: the softmax reference must move
+    many times inside a segment and the partials' maxima differ by up to ~200."""
+    _say(f"climbing scores {qd}/{cd} hq={hq} hkv={hkv} D={D} partition={part}")
+    cfg = _cfg(q_dtype=qd, cache_dtype=cd, num_heads=hq, num_kv_heads=hkv, head_dim=D,
+               len_args=(700, 17, 1, 330, 2100), seed=77)
+    wh = synth.make_workload(cfg)
+    _climbing_keys(wh, 200.0)
+    w = to_device(wh)
+    out = gpu_step(w, part)
+    ref = oracle_decode(wh, oracle_caches(wh))
+    assert_close(out, ref, cd, f"climbing {qd}/{cd} {hq}/{hkv}")
