@@ -102,7 +102,7 @@ def measured_traffic(workload):
 
 
 def time_workload(name, steps, warmup, replicas, snapshot=False, partition_size=None, use_graphs=False, window=0,
-                  q_len=1):
+                  q_len=1, shared_prefix=False):
     import torch
     import paged_kv_cache_187_amd as pa
     import synth
@@ -130,6 +130,12 @@ def time_workload(name, steps, warmup, replicas, snapshot=False, partition_size=
         n = pa.load_library().pa_decode_multi_workspace_bytes(cfg.num_seqs, q_len, cfg.num_heads, cfg.num_kv_heads,
                                                              cfg.head_dim, max_len, part)
         ws = torch.empty(n, dtype=torch.uint8, device="cuda") if n else None
+    elif shared_prefix:   # the beams of one prompt form a group sharing its prefix blocks
+        query = w.query
+        prefix = torch.full((cfg.num_seqs // cfg.beams,), cfg.prefix_len // 16, dtype=torch.int32, device="cuda")
+        n = pa.shared_prefix_workspace_bytes(cfg.num_seqs, cfg.beams, cfg.num_heads, cfg.num_kv_heads, cfg.head_dim,
+                                             max_len)
+        ws = torch.empty(n, dtype=torch.uint8, device="cuda") if n else None
     else:
         query = w.query
         ws = pa.alloc_workspace(w.query, cfg.num_kv_heads, w.max_context_len, part)
@@ -142,6 +148,9 @@ def time_workload(name, steps, warmup, replicas, snapshot=False, partition_size=
         if q_len > 1:
             pa.pa_decode_multi(out, query, kcs[r], vcs[r], w.block_tables, w.context_lens, cfg.scale, max_len,
                                partition_size=part, k_scale=kss[r], v_scale=vss[r], workspace=ws)
+        elif shared_prefix:
+            pa.pa_decode_shared_prefix(out, w.query, kcs[r], vcs[r], w.block_tables, w.context_lens, prefix,
+                                       cfg.beams, cfg.scale, max_len, k_scale=kss[r], v_scale=vss[r], workspace=ws)
         elif window > 0:
             pa.pa_decode_sliding(out, w.query, kcs[r], vcs[r], w.block_tables, w.context_lens, cfg.scale, max_len,
                                  window, partition_size=part, k_scale=kss[r], v_scale=vss[r], workspace=ws)
@@ -332,7 +341,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama7b")
     ap.add_argument("--replicas", type=int, default=3, help="pool replicas rotated across steps")
-    ap.add_argument("--also", default="gqa70b", help="comma-separated extra workloads reported alongside")
+    ap.add_argument("--also", default="gqa70b,fp8beams", help="comma-separated extra workloads reported alongside "
+                    "(a workload with shared-prefix beams is also timed through pa_decode_shared_prefix)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graphs", action="store_true", help="replay captured HIP graphs of each replica's append "
@@ -368,6 +378,7 @@ def main():
         return
 
     import paged_kv_cache_187_amd as pa
+    import synth
     pa.load_library()
 
     main_r = time_workload(args.workload, args.steps, args.warmup, args.replicas,
@@ -383,6 +394,12 @@ def main():
         also[name]["traffic"] = measured_traffic(name)
         del r
         torch.cuda.empty_cache()
+        if synth.CONFIGS[name].beams > 1:
+            r = time_workload(name, args.steps, args.warmup, args.replicas, use_graphs=args.graphs,
+                              shared_prefix=True)
+            also[f"{name}_shared_prefix"] = summarize(name, r)
+            del r
+            torch.cuda.empty_cache()
 
     if args.multi > 1:
         r = time_workload(args.workload, args.steps, args.warmup, args.replicas, partition_size=args.partition_size,

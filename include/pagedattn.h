@@ -289,6 +289,45 @@ size_t pa_decode_multi_workspace_bytes(int32_t num_seqs, int32_t q_len, int32_t 
                                        int32_t num_kv_heads, int32_t head_dim,
                                        int32_t max_context_len, int32_t partition_size);
 
+/* pa_decode_shared_prefix - paged decode for groups of sequences that share a prefix.
+ *
+ * Beam search and parallel sampling give several sequences the same prefix blocks,
+ * shared through reference counts ("LLM推理引擎深度实战：从PagedAttention到分布式推理部署",
+ * §2.2, copy-on-write; "大模型推理引擎优化：KV Cache 与连续批处理", §三 and §4.2).  The
+ * result is exactly pa_decode's (up to rounding order): every sequence attends to its
+ * own L_b tokens through its own page table.  What differs is the reading: sequences
+ * g*group_size .. g*group_size + group_size - 1 form group g, and the first
+ * prefix_blocks[g] page-table entries of group g are read once for all of its
+ * sequences, whose query heads of one KV head fill the rows of one 16-row
+ * matrix-core tile.
+ *
+ * prefix_blocks : int32 [num_seqs / group_size] on the device.  Caller contract: the
+ *                 first prefix_blocks[g] entries of the tables of group g are equal
+ *                 (values are clamped to [0, shortest sequence's block count]; a
+ *                 wrong claim gives undefined results for that group, never an
+ *                 out-of-pool access).
+ * group_size    : 1..16, dividing num_seqs, with group_size * (num_heads /
+ *                 num_kv_heads) <= 16; otherwise PA_ERR_SHAPE.
+ * Always the balanced split (no partition_size); the workspace size comes from
+ * pa_decode_shared_prefix_workspace_bytes.  Every other argument is as for pa_decode.
+ */
+pa_status pa_decode_shared_prefix(void *out, const void *query,
+                                  const void *key_cache, const void *value_cache,
+                                  const float *k_scale, const float *v_scale,
+                                  const int32_t *block_tables, const int32_t *context_lens,
+                                  const int32_t *prefix_blocks, int32_t group_size,
+                                  int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int64_t num_blocks,
+                                  int32_t max_blocks_per_seq, int32_t max_context_len,
+                                  float scale, int32_t q_dtype, int32_t cache_dtype,
+                                  void *workspace, size_t workspace_bytes, void *stream);
+
+/* pa_decode_shared_prefix_workspace_bytes - workspace pa_decode_shared_prefix needs
+ * ((size_t)-1: invalid shape). */
+size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t group_size,
+                                               int32_t num_heads, int32_t num_kv_heads,
+                                               int32_t head_dim, int32_t max_context_len);
+
 /* pa_status_string - static, human-readable name of a status code. */
 const char *pa_status_string(int32_t status);
 

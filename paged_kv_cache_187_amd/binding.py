@@ -62,6 +62,11 @@ def load_library(path=LIB_PATH):
     lib.pa_decode_multi.restype = i32
     lib.pa_decode_multi_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     lib.pa_decode_multi_workspace_bytes.restype = sz
+    lib.pa_decode_shared_prefix.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i64, i32,
+                                             i32, ctypes.c_float, i32, i32, vp, sz, vp]
+    lib.pa_decode_shared_prefix.restype = i32
+    lib.pa_decode_shared_prefix_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.pa_decode_shared_prefix_workspace_bytes.restype = sz
     lib.pa_status_string.argtypes = [i32]
     lib.pa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -250,3 +255,45 @@ def pa_decode_multi(out, query, key_cache, value_cache, block_tables, context_le
         int(max_context_len), float(scale), int(partition_size), _DTYPE[query.dtype], _DTYPE[key_cache.dtype],
         _ptr(workspace), ws_bytes, _stream(stream)))
     return out
+
+
+def pa_decode_shared_prefix(out, query, key_cache, value_cache, block_tables, context_lens, prefix_blocks,
+                            group_size, scale, max_context_len, k_scale=None, v_scale=None, workspace=None,
+                            stream=None):
+    """pa_decode for groups of ``group_size`` consecutive sequences whose first
+    ``prefix_blocks[g]`` page-table entries are shared: those blocks are read once per group.
+
+    prefix_blocks: int32 [B / group_size] on the device.  The result is pa_decode's.
+    """
+    _on_gpu(out, query, key_cache, value_cache, block_tables, context_lens, prefix_blocks, k_scale, v_scale,
+            workspace)
+    B, hq, d = query.shape
+    nb, bs, hkv, dk = key_cache.shape
+    if out.shape != query.shape or out.dtype != query.dtype or bs != BLOCK_SIZE or dk != d or \
+            value_cache.shape != key_cache.shape or block_tables.dim() != 2 or \
+            block_tables.shape[0] != B or context_lens.shape != (B,) or group_size < 1 or B % group_size or \
+            prefix_blocks.shape != (B // group_size,) or block_tables.dtype != torch.int32 or \
+            context_lens.dtype != torch.int32 or prefix_blocks.dtype != torch.int32:
+        raise ValueError("inconsistent shapes for pa_decode_shared_prefix")
+    lib = load_library()
+    if workspace is None:
+        n = lib.pa_decode_shared_prefix_workspace_bytes(B, int(group_size), hq, hkv, d, int(max_context_len))
+        if n == ctypes.c_size_t(-1).value:
+            raise PagedAttnError(2, "invalid arguments for pa_decode_shared_prefix_workspace_bytes")
+        workspace = torch.empty(n, dtype=torch.uint8, device=query.device) if n else None
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.pa_decode_shared_prefix(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(k_scale), _ptr(v_scale),
+        _ptr(block_tables), _ptr(context_lens), _ptr(prefix_blocks), int(group_size), B, hq, hkv, d, nb,
+        block_tables.shape[1], int(max_context_len), float(scale), _DTYPE[query.dtype], _DTYPE[key_cache.dtype],
+        _ptr(workspace), ws_bytes, _stream(stream)))
+    return out
+
+
+def shared_prefix_workspace_bytes(num_seqs, group_size, num_heads, num_kv_heads, head_dim, max_context_len):
+    """Bytes of workspace pa_decode_shared_prefix needs."""
+    n = load_library().pa_decode_shared_prefix_workspace_bytes(num_seqs, group_size, num_heads, num_kv_heads,
+                                                              head_dim, max_context_len)
+    if n == ctypes.c_size_t(-1).value:
+        raise PagedAttnError(2, "invalid arguments for pa_decode_shared_prefix_workspace_bytes")
+    return n

@@ -34,22 +34,31 @@ struct Plan {
     int64_t slots;       // workspace slots (each HPW heads x (D + 2) floats)
 };
 
+// seq_group > 0: shared-prefix groups of seq_group consecutive sequences, each unit holding
+// the group's sequences times the query heads of one KV head as rows of a 16-row tile.
 Plan make_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
-               int32_t max_context_len, int32_t partition_size, int32_t q_len = 1) {
+               int32_t max_context_len, int32_t partition_size, int32_t q_len = 1, int32_t seq_group = 0) {
     Plan pl{};
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 || head_dim <= 0 ||
         max_context_len < 0 || partition_size < 0 || partition_size % PA_BLOCK_SIZE != 0 ||
-        partition_size > kMaxPartition || q_len < 1 || q_len > kMaxQueries)
+        partition_size > kMaxPartition || q_len < 1 || q_len > kMaxQueries || seq_group < 0)
         return pl;
-    const pa::HeadGrouping hg = q_len == 1 ? pa::head_grouping(num_heads / num_kv_heads)
-                                           : pa::multi_query_grouping(num_heads / num_kv_heads);
+    const int32_t group = num_heads / num_kv_heads;
+    if (seq_group > 0 &&
+        (q_len != 1 || partition_size != 0 || num_seqs % seq_group != 0 || (int64_t)seq_group * group > 16))
+        return pl;
+    const pa::HeadGrouping hg = seq_group > 0 ? pa::HeadGrouping{group, true}
+                                : q_len == 1  ? pa::head_grouping(group)
+                                              : pa::multi_query_grouping(group);
     pl.hpw = hg.hpw;
     pl.mfma = hg.mfma;
-    pl.qpw = q_len == 1 ? 1 : std::min<int64_t>(q_len, 16 / pl.hpw);
-    pl.qgroups = (q_len + pl.qpw - 1) / pl.qpw;
+    pl.qpw = seq_group > 0 ? seq_group : q_len == 1 ? 1 : std::min<int64_t>(q_len, 16 / pl.hpw);
+    pl.qgroups = seq_group > 0 ? 1 : (q_len + pl.qpw - 1) / pl.qpw;
     pl.groups = num_heads / pl.hpw * pl.qgroups;
-    const int64_t seq_groups = (int64_t)num_seqs * pl.groups;
-    const int64_t max_blocks = (max_context_len + PA_BLOCK_SIZE - 1) / PA_BLOCK_SIZE;
+    const int64_t entries = seq_group > 0 ? num_seqs / seq_group : num_seqs;
+    const int64_t seq_groups = entries * pl.groups;
+    const int64_t max_blocks = (max_context_len + PA_BLOCK_SIZE - 1) / PA_BLOCK_SIZE *
+                               (seq_group > 0 ? seq_group : 1);   // per entry
     if (seq_groups * (max_blocks > 0 ? max_blocks : 1) >= kMaxWork) return pl;
     pl.balanced = partition_size == 0;
     if (pl.balanced) {
@@ -123,7 +132,8 @@ pa_status decode_impl(void* out, const void* query, const void* key_cache, const
                     const int32_t* context_lens, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                     int32_t head_dim, int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
                     float scale, int32_t partition_size, int32_t q_dtype, int32_t cache_dtype, void* workspace,
-                    size_t workspace_bytes, void* stream, int32_t window, int32_t q_len) {
+                    size_t workspace_bytes, void* stream, int32_t window, int32_t q_len,
+                    int32_t seq_group = 0, const int32_t* prefix_blocks = nullptr) {
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 ||
         num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || num_heads > 65536)
         return PA_ERR_SHAPE;
@@ -132,15 +142,18 @@ pa_status decode_impl(void* out, const void* query, const void* key_cache, const
     const bool fp8 = cache_dtype == PA_FP8_E4M3;
     if (!fp8 && cache_dtype != q_dtype) return PA_ERR_DTYPE;
     if (!std::isfinite(scale) || window < 0) return PA_ERR_SHAPE;
-    const Plan pl = make_plan(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, partition_size, q_len);
+    const Plan pl = make_plan(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, partition_size, q_len,
+                              seq_group);
     if (!pl.ok) return PA_ERR_SHAPE;
     const size_t need = workspace_size(pl, head_dim);
     if (num_seqs == 0) return PA_OK;
     if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens) return PA_ERR_NULL;
+    if (seq_group > 0 && !prefix_blocks) return PA_ERR_NULL;
     if (fp8 && (!k_scale || !v_scale)) return PA_ERR_NULL;
     if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
     if (!aligned(out, 16) || !aligned(query, 16) || !aligned(key_cache, 16) || !aligned(value_cache, 16) ||
         !aligned(block_tables, 4) || !aligned(context_lens, 4) || (need > 0 && !aligned(workspace, 16)) ||
+        (seq_group > 0 && !aligned(prefix_blocks, 4)) ||
         (fp8 && (!aligned(k_scale, 16) || !aligned(v_scale, 16))))
         return PA_ERR_ALIGN;
 
@@ -177,6 +190,8 @@ pa_status decode_impl(void* out, const void* query, const void* key_cache, const
     p.num_waves = (int32_t)pl.waves;
     p.window = window;
     p.scale_log2 = scale * 1.4426950408889634f;
+    p.sgroup = seq_group;
+    p.prefix_blocks = seq_group > 0 ? prefix_blocks : nullptr;
     return from_hip(pa::launch_decode(p, head_dim, q_dtype, cache_dtype, (hipStream_t)stream));
 }
 
@@ -312,6 +327,27 @@ pa_status pa_decode_multi(void* out, const void* query, const void* key_cache, c
     return decode_impl(out, query, key_cache, value_cache, k_scale, v_scale, block_tables, context_lens, num_seqs,
                        num_heads, num_kv_heads, head_dim, num_blocks, max_blocks_per_seq, max_context_len, scale,
                        partition_size, q_dtype, cache_dtype, workspace, workspace_bytes, stream, 0, q_len);
+}
+
+pa_status pa_decode_shared_prefix(void* out, const void* query, const void* key_cache, const void* value_cache,
+                                  const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                                  const int32_t* context_lens, const int32_t* prefix_blocks, int32_t group_size,
+                                  int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                                  float scale, int32_t q_dtype, int32_t cache_dtype, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+    if (group_size < 1 || group_size > 16) return PA_ERR_SHAPE;
+    return decode_impl(out, query, key_cache, value_cache, k_scale, v_scale, block_tables, context_lens, num_seqs,
+                       num_heads, num_kv_heads, head_dim, num_blocks, max_blocks_per_seq, max_context_len, scale, 0,
+                       q_dtype, cache_dtype, workspace, workspace_bytes, stream, 0, 1, group_size, prefix_blocks);
+}
+
+size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t group_size, int32_t num_heads,
+                                               int32_t num_kv_heads, int32_t head_dim, int32_t max_context_len) {
+    if (group_size < 1 || group_size > 16) return (size_t)-1;
+    const Plan pl = make_plan(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, 0, 1, group_size);
+    if (!pl.ok) return (size_t)-1;
+    return workspace_size(pl, head_dim);
 }
 
 size_t pa_decode_multi_workspace_bytes(int32_t num_seqs, int32_t q_len, int32_t num_heads, int32_t num_kv_heads,

@@ -87,26 +87,52 @@ __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
     return x;
 }
 
-// Blocks of all sequences together (the same value in every lane).
+// Shared-prefix groups.  The prefix of group gi is its first prefix_blocks[gi] blocks,
+// clamped to the shortest sequence of the group (every sequence holds all of them).
+// Blocks a unit of group gi reads: the shared prefix once, then every sequence's blocks
+// after it.  (At most 16 sequences per group: the loads are issued together.)
+__device__ int group_blocks(const DecodeParams& p, int gi) {
+    int nb[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s) nb[s] = s < p.sgroup ? seq_blocks(p, gi * p.sgroup + s) : 0;
+    const int P0 = p.prefix_blocks[gi];
+    int sum = 0, mn = 0x7fffffff;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+        sum += nb[s];
+        if (s < p.sgroup) mn = min(mn, nb[s]);
+    }
+    const int P = P0 < 0 ? 0 : (P0 > mn ? mn : P0);
+    return sum - (p.sgroup - 1) * P;
+}
+
+// Entries of the balanced order: sequences, or shared-prefix groups of sequences.
+__device__ __forceinline__ int num_entries(const DecodeParams& p) { return p.sgroup > 0 ? p.B / p.sgroup : p.B; }
+__device__ __forceinline__ int entry_blocks(const DecodeParams& p, int e) {
+    return p.sgroup > 0 ? group_blocks(p, e) : seq_blocks(p, e);
+}
+
+// Blocks of all entries together (the same value in every lane).
 __device__ int total_blocks(const DecodeParams& p, int lane) {
+    const int n = num_entries(p);
     int total = 0;
-    for (int c = 0; c < p.B; c += kWave) {
+    for (int c = 0; c < n; c += kWave) {
         const int b = c + lane;
-        const int incl = wave_incl_scan(b < p.B ? seq_blocks(p, b) : 0, lane);
+        const int incl = wave_incl_scan(b < n ? entry_blocks(p, b) : 0, lane);
         total += __builtin_amdgcn_readlane(incl, kWave - 1);
     }
     return total;
 }
 
 struct SeqPos {
-    int b;       // sequence
-    int start;   // blocks of all earlier sequences
-    int nblk;    // blocks of this sequence
+    int b;       // entry: sequence, or shared-prefix group
+    int start;   // blocks of all earlier entries
+    int nblk;    // blocks of this entry
 };
 
-// Block counts of the sequences, read once per wave: lane b holds sequence b's
-// block count and exclusive block prefix when there are at most 64 sequences
-// (`single`); otherwise the lookups below walk the lengths 64 at a time.
+// Block counts of the entries, read once per wave: lane b holds entry b's block count
+// and exclusive block prefix when there are at most 64 entries (`single`); otherwise
+// the lookups below walk the lengths 64 at a time.
 struct SeqTable {
     int nb, start, total;
     bool single;
@@ -114,27 +140,28 @@ struct SeqTable {
 
 __device__ SeqTable seq_table(const DecodeParams& p, int lane) {
     SeqTable st;
-    st.single = p.B <= kWave;
-    st.nb = lane < p.B ? seq_blocks(p, lane) : 0;
+    const int n = num_entries(p);
+    st.single = n <= kWave;
+    st.nb = lane < n ? entry_blocks(p, lane) : 0;
     const int incl = wave_incl_scan(st.nb, lane);
     st.start = incl - st.nb;
     st.total = st.single ? __builtin_amdgcn_readlane(incl, kWave - 1) : total_blocks(p, lane);
     return st;
 }
 
-// The non-empty sequence holding balanced-order position pos, where the
-// position of (b, hg, j) is groups * start_b + hg * nblk_b + j and
-// 0 <= pos < groups * total_blocks.
+// The non-empty entry holding balanced-order position pos, where the position of
+// (b, hg, j) is groups * start_b + hg * nblk_b + j and 0 <= pos < groups * total_blocks.
 __device__ SeqPos locate(const DecodeParams& p, const SeqTable& st, int lane, int pos) {
     if (st.single) {
         const uint64_t mask = __ballot(st.nb > 0 && p.groups * st.start <= pos);
         const int lb = 63 - __builtin_clzll(mask);
         return {lb, __builtin_amdgcn_readlane(st.start, lb), __builtin_amdgcn_readlane(st.nb, lb)};
     }
+    const int n = num_entries(p);
     int carry = 0;
-    for (int c = 0; c < p.B; c += kWave) {
+    for (int c = 0; c < n; c += kWave) {
         const int b = c + lane;
-        const int nb = b < p.B ? seq_blocks(p, b) : 0;
+        const int nb = b < n ? entry_blocks(p, b) : 0;
         const int incl = wave_incl_scan(nb, lane);
         const int start = carry + incl - nb;
         const uint64_t mask = __ballot(nb > 0 && p.groups * start <= pos);
@@ -148,13 +175,14 @@ __device__ SeqPos locate(const DecodeParams& p, const SeqTable& st, int lane, in
     return {0, 0, 0};
 }
 
-// Block count and exclusive block prefix of sequence b (b wave-uniform).
+// Block count and exclusive block prefix of entry b (b wave-uniform).
 __device__ SeqPos seq_entry(const DecodeParams& p, const SeqTable& st, int lane, int b) {
     if (st.single) return {b, __builtin_amdgcn_readlane(st.start, b), __builtin_amdgcn_readlane(st.nb, b)};
+    const int n = num_entries(p);
     int carry = 0;
-    for (int c = 0; c < p.B; c += kWave) {
+    for (int c = 0; c < n; c += kWave) {
         const int bb = c + lane;
-        const int nb = bb < p.B ? seq_blocks(p, bb) : 0;
+        const int nb = bb < n ? entry_blocks(p, bb) : 0;
         const int incl = wave_incl_scan(nb, lane);
         if (b < c + kWave)
             return {b, carry + __builtin_amdgcn_readlane(incl - nb, b - c), __builtin_amdgcn_readlane(nb, b - c)};
@@ -175,10 +203,15 @@ struct Ranges {
     __device__ int range_of(int pos) const { return pos / C; }
 };
 
+// Shared-prefix groups write 16-row partials, so their ranges are at least this long
+// (short ranges cost more in partials and per-range start-up than they gain in waves).
+constexpr int kMinGroupRange = 16;
+
 __device__ Ranges make_ranges(const DecodeParams& p, int T) {
     Ranges r;
     r.T = T;
     r.C = T > 0 ? (T + p.num_waves - 1) / p.num_waves : 1;
+    if (p.sgroup > 0 && r.C < kMinGroupRange) r.C = kMinGroupRange;
     return r;
 }
 
@@ -587,16 +620,34 @@ struct MfmaSegment {
         const int g = lane >> 4;
         // Row of this lane's softmax column: its query, and the last token that query sees
         // (new token qi sits at position L - qlen + qi and attends to tokens up to there).
+        // With shared-prefix groups the rows are the group's sequences b + qi instead (one
+        // query each, attending to all of its L_qi tokens).
+        const bool grouped = p.sgroup > 0;
         const int qi = q0 + c / G;
-        const bool row_ok = c < p.rows && qi < p.qlen;
-        const int last = L - p.qlen + qi;
+        const bool row_ok = c < p.rows && qi < (grouped ? p.sgroup : p.qlen);
+        // Groups: lane s < sgroup holds the length of the group's sequence s, lane sgroup the
+        // group's prefix claim (one load for the wave).
+        int glen = 0;
+        if (grouped) {
+            if (lane < p.sgroup) glen = seq_len(p, b + lane);
+            else if (lane == p.sgroup) glen = p.prefix_blocks[b / p.sgroup];
+        }
+        const int rowL = grouped ? (row_ok ? __shfl(glen, qi) : 0) : L;
+        const int last = grouped ? rowL - 1 : L - p.qlen + qi;
 
+        // The blocks are streamed in runs, each from one page table with one set of rows
+        // reading them: a single run for ungrouped units; for a group, the shared prefix
+        // (every row) followed by each sequence's own blocks (that sequence's rows).
+        // run_on: this lane's row reads the run; run_lv: tokens below it hold data that
+        // some row of the run reads (V rows at or past it are zeroed).
         const int32_t* table = p.block_tables + (int64_t)b * p.max_blocks;
+        bool run_on = true;
+        int run_lv = L;
         auto table_chunk = [&](int jbase) {
             const int j = jbase + lane;
             return j < p.max_blocks ? table[j] : -1;
         };
-        int tbl = table_chunk(jb);
+        int tbl = grouped ? 0 : table_chunk(jb);
 
         // Q as the B operand: lane l holds Q[row c][dk(s, g) + i]; zero for rows past the unit.
         uint4 qb[KSTEPS];
@@ -683,8 +734,8 @@ struct MfmaSegment {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = j * kBlockSize + 4 * g + r;
-                valid[r] = t >= lo && t < L;
-                seen[r] = valid[r] && t <= last;
+                valid[r] = t >= lo && t < run_lv;
+                seen[r] = run_on && t >= lo && t < rowL && t <= last;
                 const float f = kFp8 ? p.scale_log2 * ksc[r] : p.scale_log2;
                 sc[r] = seen[r] ? S[r] * f : kNegInf;
             }
@@ -750,7 +801,47 @@ struct MfmaSegment {
             }
         };
 
-        stream_blocks<NB, Buf>(jb, je, tbl, table_chunk, issue, consume);
+        // Group units: [jb, je) are positions in the unit's order, the prefix blocks 0 .. P-1
+        // and then the blocks P .. n_s - 1 of each sequence s of the group in turn.
+        int P = 0, lmax = 0;
+        if (grouped) {
+            int mn = 0x7fffffff;
+            for (int s = 0; s < p.sgroup; ++s) {
+                const int Ls = __builtin_amdgcn_readlane(glen, s);
+                mn = min(mn, (Ls + kBlockSize - 1) / kBlockSize);
+                lmax = max(lmax, Ls);
+            }
+            const int P0 = __builtin_amdgcn_readlane(glen, p.sgroup);
+            P = P0 < 0 ? 0 : (P0 > mn ? mn : P0);
+        }
+        // One run per pass: its blocks [j0, j1), page table, rows and valid-token bound.
+        for (int o = jb; o < je;) {
+            int j0 = o, j1 = je;
+            if (grouped) {
+                if (o < P) {
+                    j1 = min(P, je);
+                    table = p.block_tables + (int64_t)b * p.max_blocks;
+                    run_on = true;
+                    run_lv = lmax;
+                } else {
+                    int base = P, s = 0, Ls = 0, n = 0;
+                    for (; s < p.sgroup; ++s, base += n) {
+                        Ls = __builtin_amdgcn_readlane(glen, s);
+                        n = (Ls + kBlockSize - 1) / kBlockSize - P;
+                        if (o < base + n) break;
+                    }
+                    if (s == p.sgroup) break;      // unreachable: positions end with the last sequence
+                    j0 = P + (o - base);
+                    j1 = P + min(n, je - base);
+                    table = p.block_tables + (int64_t)(b + s) * p.max_blocks;
+                    run_on = row_ok && qi == s;
+                    run_lv = Ls;
+                }
+                tbl = table_chunk(j0);
+            }
+            stream_blocks<NB, Buf>(j0, j1, tbl, table_chunk, issue, consume);
+            o += j1 - j0;
+        }
 
         // Totals per row (lane groups hold disjoint tokens), then per output row 4g + r.
         const float ltot = group_sum(lsum);
@@ -760,8 +851,8 @@ struct MfmaSegment {
         for (int r = 0; r < 4; ++r) {
             const int row = 4 * g + r;
             const float lr = __shfl(ltot, row);
-            const int rq = q0 + row / G;               // query and head of this output row
-            if (row >= R || rq >= p.qlen) continue;
+            const int rq = q0 + row / G;               // query (or group sequence) and head of this output row
+            if (row >= R || rq >= (grouped ? p.sgroup : p.qlen)) continue;
             const int head = h0 + row % G;
             if (whole) {
                 const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
@@ -826,13 +917,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeParams p) 
         const SeqPos sp = locate(p, st, lane, pos);
         const int off = pos - p.groups * sp.start;
         const int hg = off / sp.nblk;
-        const int L = seq_len(p, sp.b);
+        // entry sp.b: a sequence, or the group of sequences sp.b * sgroup .. (whose segment
+        // resolves its own lengths)
+        const int b = p.sgroup > 0 ? sp.b * p.sgroup : sp.b;
+        const int L = p.sgroup > 0 ? 0 : seq_len(p, sp.b);
         const int lo = first_token(p, L);
         const int j0 = lo / kBlockSize;
         const int jb = j0 + off % sp.nblk;
         const int je = min(j0 + sp.nblk, jb + (pos_end - pos));
         const int s = sp.b * p.groups + hg;
-        Segment::run(p, lane, sp.b, hg, jb, je, j0, j0 + sp.nblk, lo, L, (int64_t)w + s);
+        Segment::run(p, lane, b, hg, jb, je, j0, j0 + sp.nblk, lo, L, (int64_t)w + s);
         pos += je - jb;
     }
 }
@@ -864,11 +958,13 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodePara
     const int64_t per_seq = (int64_t)p.qlen * p.Hq;
     if (row >= (int64_t)p.B * per_seq) return;
     const int b = (int)(row / per_seq);
-    const int qi = (int)(row % per_seq) / p.Hq;       // query (new token) of the row
     const int h = (int)(row % per_seq) % p.Hq;
+    // query (new token) of the row; with shared-prefix groups, the row's place in its group
+    const int qi = p.sgroup > 0 ? b % p.sgroup : (int)(row % per_seq) / p.Hq;
+    const int ent = p.sgroup > 0 ? b / p.sgroup : b;   // entry of the balanced order
     const int u = (h / p.hpw) * p.qgroups + qi / p.qpw;   // unit of (head group, query group)
     const int hh = (qi % p.qpw) * p.hpw + h % p.hpw;      // row within the unit's slots
-    const int64_t s = (int64_t)b * p.groups + u;
+    const int64_t s = (int64_t)ent * p.groups + u;
     uint16_t* orow = (uint16_t*)p.out + row * D;
 
     int64_t first;
@@ -882,7 +978,7 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodePara
     } else {
         const SeqTable st = seq_table(p, lane);
         const Ranges rg = make_ranges(p, p.groups * st.total);
-        const SeqPos e = seq_entry(p, st, lane, b);
+        const SeqPos e = seq_entry(p, st, lane, ent);
         if (e.nblk == 0) {
 #pragma unroll
             for (int k = 0; k < EPT; ++k) orow[k * kWave + lane] = to_bits(QT{}, 0.0f);

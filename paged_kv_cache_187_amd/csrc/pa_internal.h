@@ -36,6 +36,11 @@ struct DecodeParams {
     int32_t num_waves;         // waves in the grid
     int32_t window;            // sliding window in tokens (0: attend to the whole context)
     float scale_log2;          // softmax scale * log2(e)
+    // Shared-prefix groups (matrix-core path, balanced split): sequences g*sgroup ..
+    // g*sgroup + sgroup - 1 form group g and share their first prefix_blocks[g] page-table
+    // entries; a unit holds the group's sequences as tile rows.  sgroup == 0: no groups.
+    int32_t sgroup;
+    const int32_t* prefix_blocks;  // [B / sgroup]
 };
 
 hipError_t launch_append_copy(const void* key, const void* value, void* key_cache, void* value_cache,

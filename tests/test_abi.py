@@ -36,8 +36,9 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert _declared() == ["pa_append_kv", "pa_copy_blocks", "pa_decode", "pa_decode_multi",
-                           "pa_decode_multi_workspace_bytes", "pa_decode_partition_size", "pa_decode_sliding",
-                           "pa_decode_workspace_bytes", "pa_status_string", "pa_swap_blocks"]
+                           "pa_decode_multi_workspace_bytes", "pa_decode_partition_size",
+                           "pa_decode_shared_prefix", "pa_decode_shared_prefix_workspace_bytes",
+                           "pa_decode_sliding", "pa_decode_workspace_bytes", "pa_status_string", "pa_swap_blocks"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -94,6 +95,33 @@ def test_multi_query_workspace_and_checks(lib):
     st = lib.pa_decode_multi(FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, 0, 4, 8, 2, 128, 10, 4, 64, 0.1, 0,
                              F16, F16, None, 0, None)
     assert st == OK                                          # no sequences
+
+
+def test_shared_prefix_workspace_and_checks(lib):
+    bad = ctypes.c_size_t(-1).value
+    # 16 groups of 4 sequences, group of 4 heads: units = 16 groups x 8 KV heads, 16 rows each;
+    # slots = 2048 waves + 128 units
+    assert lib.pa_decode_shared_prefix_workspace_bytes(64, 4, 32, 8, 128, 1280) == (2048 + 128) * 16 * 130 * 4
+    # little work: 2 groups x 2 KV heads = 4 units of at most 2 sequences x 2 blocks: 16 waves,
+    # slots = 16 + 4, rows = 2 sequences x 2 heads
+    assert lib.pa_decode_shared_prefix_workspace_bytes(4, 2, 4, 2, 64, 20) == (16 + 4) * 4 * 66 * 4
+    assert lib.pa_decode_shared_prefix_workspace_bytes(64, 3, 32, 8, 128, 1280) == bad   # 64 % 3
+    assert lib.pa_decode_shared_prefix_workspace_bytes(64, 8, 32, 8, 128, 1280) == bad   # 8 x 4 rows > 16
+    assert lib.pa_decode_shared_prefix_workspace_bytes(64, 0, 32, 8, 128, 1280) == bad
+    assert lib.pa_decode_shared_prefix_workspace_bytes(64, 1, 34, 2, 128, 1280) == bad   # group of 17 heads
+
+    def sp(group, prefix=FAKE, **kw):
+        a = dict(B=8, Hq=8, Hkv=2, ws=FAKE, wsb=1 << 30)
+        a.update(kw)
+        return lib.pa_decode_shared_prefix(FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, prefix, group, a["B"],
+                                           a["Hq"], a["Hkv"], 128, 10, 4, 64, 0.1, F16, F16, a["ws"], a["wsb"],
+                                           None)
+    assert sp(0) == SHAPE
+    assert sp(3) == SHAPE                                    # 8 sequences in groups of 3
+    assert sp(8) == SHAPE                                    # 8 sequences x 4 heads > 16 rows
+    assert sp(4, prefix=None) == NULL
+    assert sp(4, ws=None, wsb=0) == WS
+    assert sp(4, B=0) == OK
 
 
 def test_sliding_decode_host_checks(lib):
