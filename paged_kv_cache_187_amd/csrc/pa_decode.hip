@@ -549,7 +549,9 @@ __device__ __forceinline__ float group_sum(float x) {
 // accumulators.
 constexpr float kSlack = 8.0f;
 
-template <typename QT, typename CT, int D, int NB>
+// GROUPED: units of shared-prefix groups (rows = the group's sequences x heads); the
+// ungrouped instantiation carries none of that code.
+template <typename QT, typename CT, int D, int NB, bool GROUPED>
 struct MfmaSegment {
     using M = QT;
     static constexpr int EB = Storage<CT>::bytes;
@@ -622,13 +624,13 @@ struct MfmaSegment {
         // (new token qi sits at position L - qlen + qi and attends to tokens up to there).
         // With shared-prefix groups the rows are the group's sequences b + qi instead (one
         // query each, attending to all of its L_qi tokens).
-        const bool grouped = p.sgroup > 0;
+        constexpr bool grouped = GROUPED;
         const int qi = q0 + c / G;
         const bool row_ok = c < p.rows && qi < (grouped ? p.sgroup : p.qlen);
         // Groups: lane s < sgroup holds the length of the group's sequence s, lane sgroup the
         // group's prefix claim (one load for the wave).
         int glen = 0;
-        if (grouped) {
+        if constexpr (grouped) {
             if (lane < p.sgroup) glen = seq_len(p, b + lane);
             else if (lane == p.sgroup) glen = p.prefix_blocks[b / p.sgroup];
         }
@@ -804,7 +806,7 @@ struct MfmaSegment {
         // Group units: [jb, je) are positions in the unit's order, the prefix blocks 0 .. P-1
         // and then the blocks P .. n_s - 1 of each sequence s of the group in turn.
         int P = 0, lmax = 0;
-        if (grouped) {
+        if constexpr (grouped) {
             int mn = 0x7fffffff;
             for (int s = 0; s < p.sgroup; ++s) {
                 const int Ls = __builtin_amdgcn_readlane(glen, s);
@@ -817,7 +819,7 @@ struct MfmaSegment {
         // One run per pass: its blocks [j0, j1), page table, rows and valid-token bound.
         for (int o = jb; o < je;) {
             int j0 = o, j1 = je;
-            if (grouped) {
+            if constexpr (grouped) {
                 if (o < P) {
                     j1 = min(P, je);
                     table = p.block_tables + (int64_t)b * p.max_blocks;
@@ -1080,7 +1082,9 @@ constexpr int kRing = 2;
 
 template <typename QT, typename CT, int D>
 hipError_t run_path(const DecodeParams& p, hipStream_t s) {
-    if (p.mfma) return run<QT, D, MfmaSegment<QT, CT, D, kRing>>(p, s);
+    if (p.mfma)
+        return p.sgroup > 0 ? run<QT, D, MfmaSegment<QT, CT, D, kRing, true>>(p, s)
+                            : run<QT, D, MfmaSegment<QT, CT, D, kRing, false>>(p, s);
     switch (p.hpw) {
         case 1: return run<QT, D, ValuSegment<QT, CT, D, 1, kRing>>(p, s);
         case 2: return run<QT, D, ValuSegment<QT, CT, D, 2, kRing>>(p, s);
