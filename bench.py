@@ -341,7 +341,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama7b")
     ap.add_argument("--replicas", type=int, default=3, help="pool replicas rotated across steps")
-    ap.add_argument("--also", default="gqa70b,fp8beams", help="comma-separated extra workloads reported alongside "
+    ap.add_argument("--also", default="gqa70b,fp8beams,longctx", help="comma-separated extra workloads reported alongside "
                     "(a workload with shared-prefix beams is also timed through pa_decode_shared_prefix)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -952,7 +952,9 @@ __device__ __forceinline__ float wave_sum(float x) {
 // folded in order k = 0, 1, ... with every lane holding D/64 columns.  Also
 // writes the zero rows of empty sequences in the balanced split (no segment
 // covers them).
-template <typename QT, int D>
+// LONG: lists of many partials (fixed split-K over long contexts) fold their V sums in
+// batches of loads; the short-list variant keeps fewer registers.
+template <typename QT, int D, bool LONG>
 __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeParams p) {
     constexpr int EPT = D / kWave;
     const int lane = threadIdx.x & (kWave - 1);
@@ -1054,6 +1056,23 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodePara
                 for (int e = 0; e < EPT; ++e) num[e] = __builtin_fmaf(fj, pre[j][e], num[e]);
             }
         }
+        // Long lists: the V sums of kBatch partials are loaded together, then folded in the
+        // same ascending order.
+        constexpr int kBatch = 32;
+#pragma unroll 1
+        for (; LONG && j + kBatch <= n; j += kBatch) {
+            float v[kBatch][EPT];
+#pragma unroll
+            for (int q = 0; q < kBatch; ++q)
+#pragma unroll
+                for (int e = 0; e < EPT; ++e) v[q][e] = acc[(k0 + j + q) * kstride + e * kWave];
+#pragma unroll
+            for (int q = 0; q < kBatch; ++q) {
+                const float fj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), j + q));
+#pragma unroll
+                for (int e = 0; e < EPT; ++e) num[e] = __builtin_fmaf(fj, v[q][e], num[e]);
+            }
+        }
 #pragma unroll 8
         for (; j < n; ++j) {
             const float fj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), j));
@@ -1065,14 +1084,20 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodePara
     for (int e = 0; e < EPT; ++e) orow[e * kWave + lane] = to_bits(QT{}, den > 0.0f ? num[e] / den : 0.0f);
 }
 
+// Fixed split-K with more partitions than this per sequence merges with the batched kernel.
+constexpr int kLongMerge = 48;
+
 template <typename QT, int D, typename Segment>
 hipError_t run(const DecodeParams& p, hipStream_t stream) {
     const int64_t grid = ((int64_t)p.num_waves + kWaves - 1) / kWaves;
     hipLaunchKernelGGL((decode_kernel<Segment>), dim3((uint32_t)grid), dim3(kThreads), 0, stream, p);
     if (p.balanced || p.NP > 1) {
         const int64_t rows = (int64_t)p.B * p.qlen * p.Hq;   // one merge wave per (sequence, query, head)
-        hipLaunchKernelGGL((decode_merge_kernel<QT, D>), dim3((uint32_t)((rows + kWaves - 1) / kWaves)),
-                           dim3(kThreads), 0, stream, p);
+        const dim3 grid((uint32_t)((rows + kWaves - 1) / kWaves));
+        if (!p.balanced && p.NP > kLongMerge)
+            hipLaunchKernelGGL((decode_merge_kernel<QT, D, true>), grid, dim3(kThreads), 0, stream, p);
+        else
+            hipLaunchKernelGGL((decode_merge_kernel<QT, D, false>), grid, dim3(kThreads), 0, stream, p);
     }
     return hipGetLastError();
 }
