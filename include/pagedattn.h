@@ -310,6 +310,10 @@ size_t pa_decode_multi_workspace_bytes(int32_t num_seqs, int32_t q_len, int32_t 
  *                 num_kv_heads) <= 16; otherwise PA_ERR_SHAPE.
  * Always the balanced split (no partition_size); the workspace size comes from
  * pa_decode_shared_prefix_workspace_bytes.  Every other argument is as for pa_decode.
+ * Errors (host checks only, before any launch): PA_ERR_SHAPE for a bad group size or
+ * shape; PA_ERR_NULL for a missing pointer, prefix_blocks included; PA_ERR_ALIGN when
+ * prefix_blocks is not 4-byte aligned (other buffers as for pa_decode);
+ * PA_ERR_WORKSPACE; PA_ERR_DTYPE as for pa_decode; PA_ERR_HIP on a launch failure.
  */
 pa_status pa_decode_shared_prefix(void *out, const void *query,
                                   const void *key_cache, const void *value_cache,
