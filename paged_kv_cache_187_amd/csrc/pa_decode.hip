@@ -952,9 +952,7 @@ __device__ __forceinline__ float wave_sum(float x) {
 // folded in order k = 0, 1, ... with every lane holding D/64 columns.  Also
 // writes the zero rows of empty sequences in the balanced split (no segment
 // covers them).
-// LONG: lists of many partials (fixed split-K over long contexts) fold their V sums in
-// batches of loads; the short-list variant keeps fewer registers.
-template <typename QT, int D, bool LONG>
+template <typename QT, int D>
 __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeParams p) {
     constexpr int EPT = D / kWave;
     const int lane = threadIdx.x & (kWave - 1);
@@ -1056,23 +1054,6 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodePara
                 for (int e = 0; e < EPT; ++e) num[e] = __builtin_fmaf(fj, pre[j][e], num[e]);
             }
         }
-        // Long lists: the V sums of kBatch partials are loaded together, then folded in the
-        // same ascending order.
-        constexpr int kBatch = 32;
-#pragma unroll 1
-        for (; LONG && j + kBatch <= n; j += kBatch) {
-            float v[kBatch][EPT];
-#pragma unroll
-            for (int q = 0; q < kBatch; ++q)
-#pragma unroll
-                for (int e = 0; e < EPT; ++e) v[q][e] = acc[(k0 + j + q) * kstride + e * kWave];
-#pragma unroll
-            for (int q = 0; q < kBatch; ++q) {
-                const float fj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), j + q));
-#pragma unroll
-                for (int e = 0; e < EPT; ++e) num[e] = __builtin_fmaf(fj, v[q][e], num[e]);
-            }
-        }
 #pragma unroll 8
         for (; j < n; ++j) {
             const float fj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), j));
@@ -1084,7 +1065,104 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodePara
     for (int e = 0; e < EPT; ++e) orow[e * kWave + lane] = to_bits(QT{}, den > 0.0f ? num[e] / den : 0.0f);
 }
 
-// Fixed split-K with more partitions than this per sequence merges with the batched kernel.
+// Merge of long lists of fixed partitions (split-K over long contexts): one workgroup
+// per output row.  Every wave computes the common maximum M and the denominator over
+// all partials; wave w folds the V sums of the w-th contiguous quarter of the list,
+// loading kBatch partials at a time; the quarters are added in order w = 0, 1, ...
+// through LDS, so the result is deterministic for fixed inputs.
+template <typename QT, int D>
+__global__ __launch_bounds__(kThreads) void decode_merge_split_kernel(const DecodeParams p) {
+    constexpr int EPT = D / kWave;
+    constexpr int kBatch = 16;
+    __shared__ float quarter[kWaves][D];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int64_t row = blockIdx.x;                 // grid = output rows
+    const int64_t per_seq = (int64_t)p.qlen * p.Hq;
+    const int b = (int)(row / per_seq);
+    const int qi = (int)(row % per_seq) / p.Hq;
+    const int h = (int)(row % per_seq) % p.Hq;
+    const int u = (h / p.hpw) * p.qgroups + qi / p.qpw;
+    const int hh = (qi % p.qpw) * p.hpw + h % p.hpw;
+    const int64_t s = (int64_t)b * p.groups + u;
+    const int nblk = seq_blocks(p, b);
+    const int count = (nblk + p.part_blocks - 1) / p.part_blocks;
+    if (count <= 1) return;                  // written by the one partition (the whole workgroup)
+    const int64_t first = s * p.NP;
+    const int hpw = p.rows;
+    const float* ml = p.ws_ml;
+    const float* acc = p.ws_acc + (first * hpw + hh) * D + lane;
+    const int64_t kstride = (int64_t)hpw * D;
+    auto pair = [&](int k, float& mk, float& lk) {
+        mk = kNegInf;
+        lk = 0.0f;
+        if (k < count) {
+            const int64_t hs = (first + k) * hpw + hh;
+            mk = ml[hs * 2];
+            lk = ml[hs * 2 + 1];
+        }
+    };
+
+    float M = kNegInf;
+    for (int k0 = 0; k0 < count; k0 += kWave) {
+        float mk, lk;
+        pair(k0 + lane, mk, lk);
+        M = __builtin_fmaxf(M, wave_max(mk));
+    }
+    const float ms = (M == kNegInf) ? 0.0f : M;
+    float den = 0.0f;
+    for (int k0 = 0; k0 < count; k0 += kWave) {
+        float mk, lk;
+        pair(k0 + lane, mk, lk);
+        den += wave_sum(k0 + lane < count ? fast_exp2(mk - ms) * lk : 0.0f);
+    }
+
+    const int q = (count + kWaves - 1) / kWaves;
+    const int k_lo = min(count, wv * q), k_hi = min(count, k_lo + q);
+    float num[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) num[e] = 0.0f;
+    for (int k0 = k_lo; k0 < k_hi; k0 += kWave) {
+        float mk, lk;
+        pair(k0 + lane, mk, lk);
+        const float f = k0 + lane < k_hi ? fast_exp2(mk - ms) : 0.0f;
+        const int n = min(kWave, k_hi - k0);
+        int j = 0;
+#pragma unroll 1
+        for (; j + kBatch <= n; j += kBatch) {
+            float v[kBatch][EPT];
+#pragma unroll
+            for (int t = 0; t < kBatch; ++t)
+#pragma unroll
+                for (int e = 0; e < EPT; ++e) v[t][e] = acc[(k0 + j + t) * kstride + e * kWave];
+#pragma unroll
+            for (int t = 0; t < kBatch; ++t) {
+                const float fj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), j + t));
+#pragma unroll
+                for (int e = 0; e < EPT; ++e) num[e] = __builtin_fmaf(fj, v[t][e], num[e]);
+            }
+        }
+        for (; j < n; ++j) {
+            const float fj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), j));
+#pragma unroll
+            for (int e = 0; e < EPT; ++e) num[e] = __builtin_fmaf(fj, acc[(k0 + j) * kstride + e * kWave], num[e]);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) quarter[wv][e * kWave + lane] = num[e];
+    __syncthreads();
+    if (wv != 0) return;
+    uint16_t* orow = (uint16_t*)p.out + row * D;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+        float t = quarter[0][e * kWave + lane];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) t += quarter[w][e * kWave + lane];
+        orow[e * kWave + lane] = to_bits(QT{}, den > 0.0f ? t / den : 0.0f);
+    }
+}
+
+// Fixed split-K with more partitions than this per sequence merges with the split kernel.
 constexpr int kLongMerge = 48;
 
 template <typename QT, int D, typename Segment>
@@ -1093,11 +1171,11 @@ hipError_t run(const DecodeParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((decode_kernel<Segment>), dim3((uint32_t)grid), dim3(kThreads), 0, stream, p);
     if (p.balanced || p.NP > 1) {
         const int64_t rows = (int64_t)p.B * p.qlen * p.Hq;   // one merge wave per (sequence, query, head)
-        const dim3 grid((uint32_t)((rows + kWaves - 1) / kWaves));
         if (!p.balanced && p.NP > kLongMerge)
-            hipLaunchKernelGGL((decode_merge_kernel<QT, D, true>), grid, dim3(kThreads), 0, stream, p);
+            hipLaunchKernelGGL((decode_merge_split_kernel<QT, D>), dim3((uint32_t)rows), dim3(kThreads), 0, stream, p);
         else
-            hipLaunchKernelGGL((decode_merge_kernel<QT, D, false>), grid, dim3(kThreads), 0, stream, p);
+            hipLaunchKernelGGL((decode_merge_kernel<QT, D>), dim3((uint32_t)((rows + kWaves - 1) / kWaves)),
+                               dim3(kThreads), 0, stream, p);
     }
     return hipGetLastError();
 }
