@@ -198,3 +198,14 @@ def test_shared_prefix_rejects_bad_groups():
         pa.pa_decode_shared_prefix(out, q, kc, vc, tables, lens, one, 3, c["scale"], c["max_len"])
     with pytest.raises(pa.PagedAttnError):   # 4 sequences x 8 heads = 32 rows > 16
         pa.pa_decode_shared_prefix(out, q, kc, vc, tables, lens, one, 4, c["scale"], c["max_len"])
+
+
+def test_shared_prefix_more_than_64_groups():
+    # 70 groups of 2 sequences: the balanced split walks the groups 64 at a time.
+    _say("shared prefix: 70 groups (group table walked 64 at a time)")
+    kinds = (["prefix", "none", "inside", "long", "empty_member", "all_empty", "prefix"] * 10)[:70]
+    c = _case(2, 16, 4, 64, "f16", "f16", kinds, seed=91)
+    ref = _reference(c)
+    out, plain = _gpu(c)
+    assert_close(out, ref, "f16", "shared prefix, 70 groups")
+    assert_close(plain, ref, "f16", "pa_decode on the same tables, 140 sequences")
