@@ -354,6 +354,8 @@ def main():
                     help="new tokens per sequence of the extra pa_decode_multi line on the main workload; <2 = skip")
     ap.add_argument("--window", type=int, default=512,
                     help="sliding window (tokens) of the extra pa_decode_sliding line on the main workload; 0 = skip")
+    ap.add_argument("--shared-prefix", action="store_true",
+                    help="time the main workload (one with shared-prefix beams) through pa_decode_shared_prefix")
     ap.add_argument("--partition-size", type=int, default=None,
                     help="override the workload's partition length (tokens; 0 = library's choice)")
     args = ap.parse_args()
@@ -381,9 +383,12 @@ def main():
     import synth
     pa.load_library()
 
+    if args.shared_prefix and synth.CONFIGS[args.workload].beams < 2:
+        print(f"--shared-prefix needs a workload with shared-prefix beams, not {args.workload}", file=sys.stderr)
+        sys.exit(2)
     main_r = time_workload(args.workload, args.steps, args.warmup, args.replicas,
                            snapshot=not args.no_cpu_baseline, partition_size=args.partition_size,
-                           use_graphs=args.graphs)
+                           use_graphs=args.graphs, shared_prefix=args.shared_prefix)
     s = summarize(args.workload, main_r)
     cfg = main_r["w"].cfg
     also = {}
@@ -398,6 +403,7 @@ def main():
             r = time_workload(name, args.steps, args.warmup, args.replicas, use_graphs=args.graphs,
                               shared_prefix=True)
             also[f"{name}_shared_prefix"] = summarize(name, r)
+            also[f"{name}_shared_prefix"]["traffic"] = measured_traffic(f"{name}_shared_prefix")
             del r
             torch.cuda.empty_cache()
 
@@ -449,7 +455,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": s["frac_of_peak"],
-            "traffic": measured_traffic(args.workload),
+            "traffic": measured_traffic(args.workload + ("_shared_prefix" if args.shared_prefix else "")),
             "bytes_per_launch": s["algorithmic_bytes"],
             "launch_us_mean": s["decode_us_mean"],
             "launch_us_p10_p50_p90": s["decode_us_p10_p50_p90"],
