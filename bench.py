@@ -210,6 +210,58 @@ def time_workload(name, steps, warmup, replicas, snapshot=False, partition_size=
     }
 
 
+def read_ceiling(steps=50, warmup=5):
+    """Achievable read bandwidth on this GPU, reported beside (not as) the decode figures.
+
+    stream: a plain streaming read of a 2 GiB buffer.  gather: the llama7b decode's access
+    pattern without the attention (every head's 256-byte rows of 16-token blocks of 32 KV
+    heads, blocks in random order, 2048 waves, next block's loads in flight), 4400 blocks
+    (577 MB) per launch from three disjoint block sets of a 2 GiB pool.  Probe kernels of
+    libpaprobe.so (paged_kv_cache_187_amd/probe/pa_probe.hip), timed with HIP events.
+    """
+    import ctypes
+    import torch
+    from paged_kv_cache_187_amd.build import PROBE_PATH
+    lib = ctypes.CDLL(PROBE_PATH)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.pa_probe_stream.argtypes = [vp, i64, vp, i32, vp]
+    lib.pa_probe_gather.argtypes = [vp, vp, i32, i32, i64, i32, vp, vp]
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    nbytes = 2 << 30
+    buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    hkv, n_ids, waves, blocks = 32, 4400, 2048, 4096
+    blk = 16 * hkv * 128 * 2
+    num_blocks = nbytes // blk
+    g = torch.Generator().manual_seed(7)
+    perm = torch.randperm(num_blocks, generator=g)[:3 * n_ids].to(torch.int32).cuda()
+    id_sets = [perm[i * n_ids:(i + 1) * n_ids].contiguous() for i in range(3)]
+    sink = torch.empty(max(blocks * 256, waves * 64), dtype=torch.int32, device="cuda")
+
+    def run(launch, n):
+        for i in range(warmup):
+            assert launch(i) == 0
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for i in range(n):
+            ev[i][0].record(stream)
+            assert launch(warmup + i) == 0
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) for a, b in ev)[n // 2] * 1e-3
+
+    t_stream = run(lambda i: lib.pa_probe_stream(buf.data_ptr(), nbytes, sink.data_ptr(), blocks, sp), steps)
+    t_gather = run(lambda i: lib.pa_probe_gather(buf.data_ptr(), id_sets[i % 3].data_ptr(), n_ids, hkv, num_blocks,
+                                                  waves, sink.data_ptr(), sp), steps)
+    gathered = n_ids * blk
+    del buf
+    torch.cuda.empty_cache()
+    return {"stream_read": {"bytes": nbytes, "GBs": round(nbytes / t_stream / 1e9, 1),
+                            "frac_of_peak": round(nbytes / t_stream / 1e9 / HBM_PEAK_GBS, 4)},
+            "paged_gather": {"bytes": gathered, "GBs": round(gathered / t_gather / 1e9, 1),
+                             "frac_of_peak": round(gathered / t_gather / 1e9 / HBM_PEAK_GBS, 4),
+                             "pattern": "256-byte head rows of random 16-token blocks, 32 KV heads, 2048 waves"}}
+
+
 def time_copy_blocks(steps, warmup, pairs, num_blocks=4096, replicas=2):
     """pa_copy_blocks on llama7b-shaped blocks (32 KV heads x 128 x f16: 128 KiB per pool per block).
 
@@ -350,6 +402,7 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (5 times), to scale rocprofv3 FETCH_SIZE/WRITE_SIZE")
     ap.add_argument("--no-copy", action="store_true", help="skip the pa_copy_blocks / pa_swap_blocks measurements")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the read-bandwidth ceiling probes")
     ap.add_argument("--multi", type=int, default=4,
                     help="new tokens per sequence of the extra pa_decode_multi line on the main workload; <2 = skip")
     ap.add_argument("--window", type=int, default=512,
@@ -427,6 +480,8 @@ def main():
         also["swap_blocks"] = time_swap(min(args.steps, 50), min(args.warmup, 5))
         torch.cuda.empty_cache()
 
+    ceiling = None if args.no_ceiling else read_ceiling()
+
     result = {
         "metric": METRIC,
         "value": s["tokens_per_s"],
@@ -461,6 +516,8 @@ def main():
             "launch_us_p10_p50_p90": s["decode_us_p10_p50_p90"],
         },
         "also": also,
+        # achievable read bandwidth on this machine (probe kernels), labelled apart from the decode
+        "ceiling": ceiling,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(main_r["w"], main_r["host"], args.cpu_seconds)

@@ -12,6 +12,9 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB_NAME = "libpagedattn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
+# Read-bandwidth probes (bench.py's ceiling line only; not part of the C ABI above).
+PROBE_SRC = os.path.join(PKG, "probe", "pa_probe.hip")
+PROBE_PATH = os.path.join(PKG, "libpaprobe.so")
 SOURCES = ["pa_append.hip", "pa_copy.hip", "pa_decode.hip", "pa_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
@@ -54,6 +57,9 @@ def build(verbose=False, extra_flags=()):
     tmp = LIB_PATH + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB_PATH)
+    ptmp = PROBE_PATH + ".tmp"
+    _run([HIPCC, *COMMON, *extra_flags, "-shared", "-x", "hip", PROBE_SRC, "-o", ptmp], verbose)
+    os.replace(ptmp, PROBE_PATH)
     return LIB_PATH
 
 

@@ -1,0 +1,108 @@
+// Read-bandwidth probes for gfx950, used only to report the achievable ceiling next
+// to the decode measurements (built as libpaprobe.so, not part of libpagedattn.so).
+//
+//  * pa_probe_stream: a plain streaming read of a contiguous buffer.
+//  * pa_probe_gather: the paged-decode access pattern without the attention: for every
+//    (head, position) pair, the 16 rows of one head of a block reached through an id
+//    list (rows of head_dim 16-bit values, a token row of all heads apart), in
+//    head-major order cut into equal ranges, one per wave, with the next block's loads
+//    issued before the current one is used.
+// Both XOR the loaded words into one word per lane of `sink` so the loads are kept.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+constexpr int kWave = 64;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 load_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2));
+}
+
+__global__ __launch_bounds__(256) void stream_kernel(const uint4* __restrict__ buf, int64_t n_vec,
+                                                     uint32_t* __restrict__ sink) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    uint32_t acc = 0;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_vec; i += stride) {
+        const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)buf + i);
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
+// One wave per range of (head, position) pairs; 128-element heads of 16-bit values
+// (256-byte rows: 16 lanes per row, 4 rows per load, 4 loads per 16-row block).
+__global__ __launch_bounds__(256) void gather_kernel(const char* __restrict__ pool, const int32_t* __restrict__ ids,
+                                                     int32_t n_ids, int32_t hkv, int64_t num_blocks,
+                                                     int32_t waves, uint32_t* __restrict__ sink) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = blockIdx.x * (blockDim.x / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    if (w >= waves) return;
+    const int64_t tok = (int64_t)hkv * 256;            // bytes between token rows
+    const int64_t blk = tok * 16;
+    const int64_t T = (int64_t)hkv * n_ids;
+    const int64_t C = (T + waves - 1) / waves;
+    const int64_t lo = (int64_t)w * C < T ? (int64_t)w * C : T;
+    const int64_t hi = lo + C < T ? lo + C : T;
+    const uint32_t lane_off = (uint32_t)((lane / 16) * tok + (lane % 16) * 16);
+    uint32_t acc = 0;
+    auto issue = [&](int64_t q, uint4* b) {
+        const bool ok = q < hi;
+        int64_t id = 0;
+        int head = 0;
+        if (ok) {
+            head = (int)(q / n_ids);
+            id = ids[q % n_ids];
+            if (id < 0 || id >= num_blocks) id = 0;
+        }
+        const auto r = rsrc(pool + id * blk, ok ? (int)blk : 0);
+        const uint32_t off = lane_off + (uint32_t)head * 256;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) b[i] = load_nt(r, off + (uint32_t)(i * 4 * tok));
+    };
+    uint4 a[4], b[4];
+    issue(lo, a);
+    for (int64_t q = lo; q < hi; q += 2) {
+        issue(q + 1, b);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc ^= a[i].x ^ a[i].y ^ a[i].z ^ a[i].w;
+        issue(q + 2, a);
+        if (q + 1 < hi) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc ^= b[i].x ^ b[i].y ^ b[i].z ^ b[i].w;
+        }
+    }
+    sink[(int64_t)w * kWave + lane] = acc;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Streaming read of `bytes` (a multiple of 16) from `buf`; sink holds one word per
+// thread of the grid (blocks * 256 words).  Returns a hipError_t value.
+int pa_probe_stream(const void* buf, int64_t bytes, uint32_t* sink, int32_t blocks, void* stream) {
+    if (!buf || !sink || bytes <= 0 || bytes % 16 || blocks <= 0) return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(stream_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const uint4*)buf,
+                       bytes / 16, sink);
+    return (int)hipGetLastError();
+}
+
+// Paged gather over a pool of `num_blocks` blocks [16, hkv, 128] of 16-bit values: every
+// head of every listed block, `waves` waves; sink holds waves * 64 words.
+int pa_probe_gather(const void* pool, const int32_t* ids, int32_t n_ids, int32_t hkv, int64_t num_blocks,
+                    int32_t waves, uint32_t* sink, void* stream) {
+    if (!pool || !ids || !sink || n_ids <= 0 || hkv <= 0 || num_blocks <= 0 || waves <= 0 ||
+        (int64_t)hkv * 256 * 16 > (int64_t)1 << 30)
+        return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(gather_kernel, dim3((waves + 3) / 4), dim3(256), 0, (hipStream_t)stream, (const char*)pool,
+                       ids, n_ids, hkv, num_blocks, waves, sink);
+    return (int)hipGetLastError();
+}
+
+}  // extern "C"
