@@ -383,7 +383,20 @@ def summarize(name, r):
         "effective_GBs": round(achieved, 1),
         "frac_of_peak": round(achieved / HBM_PEAK_GBS, 4),
         "partition_size": r["partition_size"],
+        **({"logical_bytes": logical_bytes(r["w"])} if cfg.beams > 1 else {}),
     }
+
+
+def logical_bytes(w):
+    """Bytes the decode requests when every sequence reads its own blocks (shared-prefix
+    blocks counted once per beam); the % of peak is quoted on the unique bytes."""
+    import numpy as np
+    cfg = w.cfg
+    eb = 1 if cfg.cache_dtype == "fp8_e4m3" else 2
+    lens = w.lens_np.astype(np.int64)
+    tokens = int(lens.sum())
+    kv = tokens * cfg.num_kv_heads * cfg.head_dim * 2 * eb + (tokens * 8 if eb == 1 else 0)
+    return kv + cfg.num_seqs * cfg.num_heads * cfg.head_dim * 2 + int(np.sum((lens + 15) // 16)) * 4 + cfg.num_seqs * 4
 
 
 def main():
