@@ -230,3 +230,16 @@ def test_binding_rejects_host_tensors():
         pa.pa_append_kv(x, x, torch.zeros(4, 16, 2, 64, dtype=torch.float16),
                         torch.zeros(4, 16, 2, 64, dtype=torch.float16), torch.zeros(2, dtype=torch.int64))
     assert ctypes.c_size_t(-1).value > 0
+
+
+def test_probe_library_exports_its_two_probes():
+    # bench.py's read-bandwidth ceiling comes from a separate library, outside the C ABI.
+    from paged_kv_cache_187_amd.build import PROBE_PATH
+    if not os.path.exists(PROBE_PATH):
+        pytest.fail("libpaprobe.so is not built (run __graft_entry__.build())")
+    nm = subprocess.run(["nm", "-D", "--defined-only", PROBE_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in nm.splitlines() if line.strip()}
+    assert {"pa_probe_stream", "pa_probe_gather"} <= exported
+    lib = ctypes.CDLL(PROBE_PATH)
+    lib.pa_probe_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+    assert lib.pa_probe_stream(None, 16, None, 1, None) != 0      # rejected on the host, nothing launched
