@@ -261,8 +261,11 @@ struct Buf {
     uint4 k[Layout<CT, D>::LPB], v[Layout<CT, D>::LPB];
     float ks[Layout<CT, D>::LPB], vs[Layout<CT, D>::LPB];
 };
+// Partials are stored where they are produced (defer is ignored; nothing to flush).
+static __device__ __forceinline__ void flush(const DecodeParams&, int, int64_t) {}
+
 static __device__ __forceinline__ void run(const DecodeParams& p, int lane, int b, int hg, int jb, int je,
-                                           int jfirst, int nblk, int lo, int L, int64_t slot) {
+                                           int jfirst, int nblk, int lo, int L, int64_t slot, bool /*defer*/) {
     using Ly = Layout<CT, D>;
     constexpr int EB = Ly::EB, EPL = Ly::EPL, TPL = Ly::TPL, ROWS = Ly::ROWS, LPB = Ly::LPB;
     constexpr bool kFp8 = EB == 1;
@@ -611,8 +614,51 @@ struct MfmaSegment {
         else return buffer_load4<kCacheStream>(r, off);
     }
 
+    // A partial that is not the wave's last result (the wave's first segment, when the unit
+    // began in an earlier range) waits in this wave's LDS stash and is written by flush()
+    // after the wave's last segment.  Stores and loads share one completion counter that
+    // retires in order, so a partial stored here would make the next segment's first loads
+    // wait for the store to be acknowledged.  Per lane: O[t][r], m, the row total, a mask.
+    static constexpr int kStash = 4 * E + 3;
+    static __device__ __forceinline__ float* stash(int lane) {
+        __shared__ float words[kWaves][kStash][kWave];
+        return &words[__builtin_amdgcn_readfirstlane(threadIdx.x / kWave)][0][lane];
+    }
+
+    // The partial stores of a segment: rows 4g + r with bit r of `rows` set, (m, l) when bit 4.
+    static __device__ __forceinline__ void store_partial(const DecodeParams& p, int lane, int64_t slot,
+                                                         const f32x4_t* O, float m, float ltot, int rows) {
+        const int c = lane & 15;
+        const int g = lane >> 4;
+        const int R = p.rows;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            if (!((rows >> r) & 1)) continue;
+            float4* arow = (float4*)(p.ws_acc + (slot * R + 4 * g + r) * D + E * c);
+#pragma unroll
+            for (int q = 0; q < E / 4; ++q)
+                arow[q] = float4{O[4 * q][r], O[4 * q + 1][r], O[4 * q + 2][r], O[4 * q + 3][r]};
+        }
+        if ((rows >> 4) & 1) {
+            p.ws_ml[(slot * R + c) * 2] = m;
+            p.ws_ml[(slot * R + c) * 2 + 1] = ltot;
+        }
+    }
+
+    // Writes the stashed partial to workspace slot `slot`.
+    static __device__ __forceinline__ void flush(const DecodeParams& p, int lane, int64_t slot) {
+        const float* st = stash(lane);
+        f32x4_t O[E];
+#pragma unroll
+        for (int t = 0; t < E; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) O[t][r] = st[(4 * t + r) * kWave];
+        store_partial(p, lane, slot, O, st[4 * E * kWave], st[(4 * E + 1) * kWave],
+                      __float_as_int(st[(4 * E + 2) * kWave]));
+    }
+
     static __device__ __forceinline__ void run(const DecodeParams& p, int lane, int b, int u, int jb, int je,
-                                               int jfirst, int nblk, int lo, int L, int64_t slot) {
+                                               int jfirst, int nblk, int lo, int L, int64_t slot, bool defer) {
         const int G = p.hpw;
         const int hg = u / p.qgroups;
         const int q0 = (u % p.qgroups) * p.qpw;        // first query of the unit
@@ -849,6 +895,27 @@ struct MfmaSegment {
         const float ltot = group_sum(lsum);
         const bool whole = jb == jfirst && je == nblk;
         const int R = p.rows;
+        if (!whole) {
+            int rows = (g == 0 && row_ok) ? 16 : 0;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 4 * g + r;
+                if (row < R && q0 + row / G < (grouped ? p.sgroup : p.qlen)) rows |= 1 << r;
+            }
+            if (!defer) {
+                store_partial(p, lane, slot, O, m, ltot, rows);
+                return;
+            }
+            float* st = stash(lane);
+#pragma unroll
+            for (int t = 0; t < E; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) st[(4 * t + r) * kWave] = O[t][r];
+            st[4 * E * kWave] = m;
+            st[(4 * E + 1) * kWave] = ltot;
+            st[(4 * E + 2) * kWave] = __int_as_float(rows);
+            return;
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = 4 * g + r;
@@ -856,29 +923,18 @@ struct MfmaSegment {
             const int rq = q0 + row / G;               // query (or group sequence) and head of this output row
             if (row >= R || rq >= (grouped ? p.sgroup : p.qlen)) continue;
             const int head = h0 + row % G;
-            if (whole) {
-                const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
-                uint32_t packed[E / 2];
+            const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
+            uint32_t packed[E / 2];
 #pragma unroll
-                for (int k = 0; k < E / 2; ++k)
-                    packed[k] = (uint32_t)to_bits(QT{}, O[2 * k][r] * inv) |
-                                ((uint32_t)to_bits(QT{}, O[2 * k + 1][r] * inv) << 16);
-                uint16_t* orow = (uint16_t*)p.out + (((int64_t)b * p.qlen + rq) * p.Hq + head) * D + E * c;
-                if constexpr (E == 8) {
-                    *(uint4*)orow = uint4{packed[0], packed[1], packed[2], packed[3]};
-                } else {
-                    *(uint2*)orow = uint2{packed[0], packed[1]};
-                }
+            for (int k = 0; k < E / 2; ++k)
+                packed[k] = (uint32_t)to_bits(QT{}, O[2 * k][r] * inv) |
+                            ((uint32_t)to_bits(QT{}, O[2 * k + 1][r] * inv) << 16);
+            uint16_t* orow = (uint16_t*)p.out + (((int64_t)b * p.qlen + rq) * p.Hq + head) * D + E * c;
+            if constexpr (E == 8) {
+                *(uint4*)orow = uint4{packed[0], packed[1], packed[2], packed[3]};
             } else {
-                float4* arow = (float4*)(p.ws_acc + (slot * R + row) * D + E * c);
-#pragma unroll
-                for (int q = 0; q < E / 4; ++q)
-                    arow[q] = float4{O[4 * q][r], O[4 * q + 1][r], O[4 * q + 2][r], O[4 * q + 3][r]};
+                *(uint2*)orow = uint2{packed[0], packed[1]};
             }
-        }
-        if (!whole && g == 0 && row_ok) {
-            p.ws_ml[(slot * R + c) * 2] = m;
-            p.ws_ml[(slot * R + c) * 2 + 1] = ltot;
         }
     }
 };
@@ -904,7 +960,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeParams p) 
         const int jb = j0 + part * p.part_blocks;
         if (jb >= nblk && !(part == 0 && nblk == 0)) return;   // L == 0: partition 0 writes zeros
         const int je = min(nblk, jb + p.part_blocks);
-        Segment::run(p, lane, b, hg, jb, je, j0, nblk, lo, L, (int64_t)s * p.NP + part);
+        Segment::run(p, lane, b, hg, jb, je, j0, nblk, lo, L, (int64_t)s * p.NP + part, false);
         return;
     }
 
@@ -913,6 +969,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeParams p) 
     const Ranges rg = make_ranges(p, p.groups * st.total);
     int pos = rg.begin(w);
     const int pos_end = rg.end(w);
+    int64_t deferred = -1;   // workspace slot of a stashed partial
     while (pos < pos_end) {
         // Position offsets count the blocks in play of (sequence, head group), which start
         // at logical block j0.
@@ -928,9 +985,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeParams p) 
         const int jb = j0 + off % sp.nblk;
         const int je = min(j0 + sp.nblk, jb + (pos_end - pos));
         const int s = sp.b * p.groups + hg;
-        Segment::run(p, lane, b, hg, jb, je, j0, j0 + sp.nblk, lo, L, (int64_t)w + s);
+        // Only a wave's first segment can end unfinished before its last one; its partial
+        // is written after the last segment (see the segment's stash).
+        const bool last = pos + (je - jb) >= pos_end;
+        const bool whole = jb == j0 && je == j0 + sp.nblk;
+        Segment::run(p, lane, b, hg, jb, je, j0, j0 + sp.nblk, lo, L, (int64_t)w + s, !last);
+        if (!last && !whole) deferred = (int64_t)w + s;
         pos += je - jb;
     }
+    if (deferred >= 0) Segment::flush(p, lane, deferred);
 }
 
 __device__ __forceinline__ float wave_max(float x) {
