@@ -210,14 +210,29 @@ def time_workload(name, steps, warmup, replicas, snapshot=False, partition_size=
     }
 
 
+def unique_blocks(name):
+    """Physical blocks holding the cached tokens of workload `name` (shared prefix blocks once),
+    from the same seeded draws as synth.make_workload, without building the pools."""
+    import numpy as np
+    from synth import workloads as W
+    cfg = W.CONFIGS[name]
+    rng = np.random.default_rng(cfg.seed)
+    lens = W.sample_lengths(cfg, rng)
+    return W.build_tables(cfg, lens, rng)[2]
+
+
 def read_ceiling(steps=50, warmup=5):
     """Achievable read bandwidth on this GPU, reported beside (not as) the decode figures.
 
-    stream: a plain streaming read of a 2 GiB buffer.  gather: the llama7b decode's access
-    pattern without the attention (every head's 256-byte rows of 16-token blocks of 32 KV
-    heads, blocks in random order, 2048 waves, next block's loads in flight), 4400 blocks
-    (577 MB) per launch from three disjoint block sets of a 2 GiB pool.  Probe kernels of
-    libpaprobe.so (paged_kv_cache_187_amd/probe/pa_probe.hip), timed with HIP events.
+    stream: a plain streaming read of a 2 GiB buffer.  paged_gather: the llama7b decode's
+    access pattern without the attention (every head's 256-byte rows of 16-token blocks of 32
+    KV heads, blocks in random order, 2048 waves, next block's loads in flight), 4400 blocks
+    (577 MB) per launch.  paged_gather_by_workload: the same probe in the geometry of the
+    gqa70b (8 KV heads, 256-byte rows) and fp8beams (8 KV heads, 128-byte rows of one-byte
+    codes) workloads, over as many block reads as the workload's K and V pools hold unique
+    blocks (the FP8 scales aside).  Each launch takes its blocks from one of three disjoint
+    sets of a 2 GiB pool.  Probe kernels of libpaprobe.so
+    (paged_kv_cache_187_amd/probe/pa_probe.hip), timed with HIP events.
     """
     import ctypes
     import torch
@@ -225,18 +240,14 @@ def read_ceiling(steps=50, warmup=5):
     lib = ctypes.CDLL(PROBE_PATH)
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     lib.pa_probe_stream.argtypes = [vp, i64, vp, i32, vp]
-    lib.pa_probe_gather.argtypes = [vp, vp, i32, i32, i64, i32, vp, vp]
+    lib.pa_probe_gather.argtypes = [vp, vp, i32, i32, i32, i64, i32, vp, vp]
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
     nbytes = 2 << 30
     buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
-    hkv, n_ids, waves, blocks = 32, 4400, 2048, 4096
-    blk = 16 * hkv * 128 * 2
-    num_blocks = nbytes // blk
-    g = torch.Generator().manual_seed(7)
-    perm = torch.randperm(num_blocks, generator=g)[:3 * n_ids].to(torch.int32).cuda()
-    id_sets = [perm[i * n_ids:(i + 1) * n_ids].contiguous() for i in range(3)]
+    waves, blocks = 2048, 4096
     sink = torch.empty(max(blocks * 256, waves * 64), dtype=torch.int32, device="cuda")
+    g = torch.Generator().manual_seed(7)
 
     def run(launch, n):
         for i in range(warmup):
@@ -249,17 +260,29 @@ def read_ceiling(steps=50, warmup=5):
         torch.cuda.synchronize()
         return sorted(a.elapsed_time(b) for a, b in ev)[n // 2] * 1e-3
 
+    def gather(hkv, row, n_ids):
+        blk = 16 * hkv * row
+        num_blocks = nbytes // blk
+        assert 3 * n_ids <= num_blocks
+        perm = torch.randperm(num_blocks, generator=g)[:3 * n_ids].to(torch.int32).cuda()
+        id_sets = [perm[i * n_ids:(i + 1) * n_ids].contiguous() for i in range(3)]
+        t = run(lambda i: lib.pa_probe_gather(buf.data_ptr(), id_sets[i % 3].data_ptr(), n_ids, hkv, row,
+                                              num_blocks, waves, sink.data_ptr(), sp), steps)
+        gathered = n_ids * blk
+        return {"bytes": gathered, "GBs": round(gathered / t / 1e9, 1),
+                "frac_of_peak": round(gathered / t / 1e9 / HBM_PEAK_GBS, 4),
+                "pattern": f"{row}-byte head rows of random 16-token blocks, {hkv} KV heads, {n_ids} block reads, "
+                           f"{waves} waves"}
+
     t_stream = run(lambda i: lib.pa_probe_stream(buf.data_ptr(), nbytes, sink.data_ptr(), blocks, sp), steps)
-    t_gather = run(lambda i: lib.pa_probe_gather(buf.data_ptr(), id_sets[i % 3].data_ptr(), n_ids, hkv, num_blocks,
-                                                  waves, sink.data_ptr(), sp), steps)
-    gathered = n_ids * blk
+    res = {"stream_read": {"bytes": nbytes, "GBs": round(nbytes / t_stream / 1e9, 1),
+                           "frac_of_peak": round(nbytes / t_stream / 1e9 / HBM_PEAK_GBS, 4)},
+           "paged_gather": gather(32, 256, 4400),
+           "paged_gather_by_workload": {"gqa70b": gather(8, 256, 2 * unique_blocks("gqa70b")),
+                                        "fp8beams": gather(8, 128, 2 * unique_blocks("fp8beams"))}}
     del buf
     torch.cuda.empty_cache()
-    return {"stream_read": {"bytes": nbytes, "GBs": round(nbytes / t_stream / 1e9, 1),
-                            "frac_of_peak": round(nbytes / t_stream / 1e9 / HBM_PEAK_GBS, 4)},
-            "paged_gather": {"bytes": gathered, "GBs": round(gathered / t_gather / 1e9, 1),
-                             "frac_of_peak": round(gathered / t_gather / 1e9 / HBM_PEAK_GBS, 4),
-                             "pattern": "256-byte head rows of random 16-token blocks, 32 KV heads, 2048 waves"}}
+    return res
 
 
 def time_copy_blocks(steps, warmup, pairs, num_blocks=4096, replicas=2):

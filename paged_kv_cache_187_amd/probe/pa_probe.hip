@@ -4,9 +4,9 @@
 //  * pa_probe_stream: a plain streaming read of a contiguous buffer.
 //  * pa_probe_gather: the paged-decode access pattern without the attention: for every
 //    (head, position) pair, the 16 rows of one head of a block reached through an id
-//    list (rows of head_dim 16-bit values, a token row of all heads apart), in
-//    head-major order cut into equal ranges, one per wave, with the next block's loads
-//    issued before the current one is used.
+//    list (128- or 256-byte rows: 128 one-byte or 16-bit values; a token row of all heads
+//    apart), in head-major order cut into equal ranges, one per wave, with the next
+//    block's loads issued before the current one is used.
 // Both XOR the loaded words into one word per lane of `sink` so the loads are kept.
 
 #include <hip/hip_runtime.h>
@@ -35,21 +35,25 @@ __global__ __launch_bounds__(256) void stream_kernel(const uint4* __restrict__ b
     sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
 }
 
-// One wave per range of (head, position) pairs; 128-element heads of 16-bit values
-// (256-byte rows: 16 lanes per row, 4 rows per load, 4 loads per 16-row block).
+// One wave per range of (head, position) pairs.  ROW-byte rows: ROW / 16 lanes per row,
+// 1024 / ROW rows per 16-byte-per-lane load, ROW / 64 loads per 16-row block.
+template <int ROW>
 __global__ __launch_bounds__(256) void gather_kernel(const char* __restrict__ pool, const int32_t* __restrict__ ids,
                                                      int32_t n_ids, int32_t hkv, int64_t num_blocks,
                                                      int32_t waves, uint32_t* __restrict__ sink) {
+    constexpr int LPR = ROW / 16;                      // lanes per row
+    constexpr int RPL = kWave / LPR;                   // rows per load
+    constexpr int NL = 16 / RPL;                       // loads per block
     const int lane = threadIdx.x & (kWave - 1);
     const int w = blockIdx.x * (blockDim.x / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     if (w >= waves) return;
-    const int64_t tok = (int64_t)hkv * 256;            // bytes between token rows
+    const int64_t tok = (int64_t)hkv * ROW;            // bytes between token rows
     const int64_t blk = tok * 16;
     const int64_t T = (int64_t)hkv * n_ids;
     const int64_t C = (T + waves - 1) / waves;
     const int64_t lo = (int64_t)w * C < T ? (int64_t)w * C : T;
     const int64_t hi = lo + C < T ? lo + C : T;
-    const uint32_t lane_off = (uint32_t)((lane / 16) * tok + (lane % 16) * 16);
+    const uint32_t lane_off = (uint32_t)((lane / LPR) * tok + (lane % LPR) * 16);
     uint32_t acc = 0;
     auto issue = [&](int64_t q, uint4* b) {
         const bool ok = q < hi;
@@ -61,20 +65,20 @@ __global__ __launch_bounds__(256) void gather_kernel(const char* __restrict__ po
             if (id < 0 || id >= num_blocks) id = 0;
         }
         const auto r = rsrc(pool + id * blk, ok ? (int)blk : 0);
-        const uint32_t off = lane_off + (uint32_t)head * 256;
+        const uint32_t off = lane_off + (uint32_t)head * ROW;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) b[i] = load_nt(r, off + (uint32_t)(i * 4 * tok));
+        for (int i = 0; i < NL; ++i) b[i] = load_nt(r, off + (uint32_t)(i * RPL * tok));
     };
-    uint4 a[4], b[4];
+    uint4 a[NL], b[NL];
     issue(lo, a);
     for (int64_t q = lo; q < hi; q += 2) {
         issue(q + 1, b);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc ^= a[i].x ^ a[i].y ^ a[i].z ^ a[i].w;
+        for (int i = 0; i < NL; ++i) acc ^= a[i].x ^ a[i].y ^ a[i].z ^ a[i].w;
         issue(q + 2, a);
         if (q + 1 < hi) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc ^= b[i].x ^ b[i].y ^ b[i].z ^ b[i].w;
+            for (int i = 0; i < NL; ++i) acc ^= b[i].x ^ b[i].y ^ b[i].z ^ b[i].w;
         }
     }
     sink[(int64_t)w * kWave + lane] = acc;
@@ -93,15 +97,21 @@ int pa_probe_stream(const void* buf, int64_t bytes, uint32_t* sink, int32_t bloc
     return (int)hipGetLastError();
 }
 
-// Paged gather over a pool of `num_blocks` blocks [16, hkv, 128] of 16-bit values: every
-// head of every listed block, `waves` waves; sink holds waves * 64 words.
-int pa_probe_gather(const void* pool, const int32_t* ids, int32_t n_ids, int32_t hkv, int64_t num_blocks,
-                    int32_t waves, uint32_t* sink, void* stream) {
+// Paged gather over a pool of `num_blocks` blocks [16, hkv, row_bytes] (row_bytes 128 or
+// 256): every head of every listed block, `waves` waves; sink holds waves * 64 words.
+// Ids outside [0, num_blocks) read block 0.  Returns a hipError_t value.
+int pa_probe_gather(const void* pool, const int32_t* ids, int32_t n_ids, int32_t hkv, int32_t row_bytes,
+                    int64_t num_blocks, int32_t waves, uint32_t* sink, void* stream) {
     if (!pool || !ids || !sink || n_ids <= 0 || hkv <= 0 || num_blocks <= 0 || waves <= 0 ||
-        (int64_t)hkv * 256 * 16 > (int64_t)1 << 30)
+        (row_bytes != 128 && row_bytes != 256) || (int64_t)hkv * row_bytes * 16 > (int64_t)1 << 30)
         return (int)hipErrorInvalidValue;
-    hipLaunchKernelGGL(gather_kernel, dim3((waves + 3) / 4), dim3(256), 0, (hipStream_t)stream, (const char*)pool,
-                       ids, n_ids, hkv, num_blocks, waves, sink);
+    const dim3 grid((waves + 3) / 4);
+    if (row_bytes == 128)
+        hipLaunchKernelGGL(gather_kernel<128>, grid, dim3(256), 0, (hipStream_t)stream, (const char*)pool, ids,
+                           n_ids, hkv, num_blocks, waves, sink);
+    else
+        hipLaunchKernelGGL(gather_kernel<256>, grid, dim3(256), 0, (hipStream_t)stream, (const char*)pool, ids,
+                           n_ids, hkv, num_blocks, waves, sink);
     return (int)hipGetLastError();
 }
 

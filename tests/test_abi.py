@@ -243,3 +243,10 @@ def test_probe_library_exports_its_two_probes():
     lib = ctypes.CDLL(PROBE_PATH)
     lib.pa_probe_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
     assert lib.pa_probe_stream(None, 16, None, 1, None) != 0      # rejected on the host, nothing launched
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.pa_probe_gather.argtypes = [vp, vp, i32, i32, i32, i64, i32, vp, vp]
+    fake = ctypes.c_void_p(256)                                       # never dereferenced: rejected first
+    for row in (0, 64, 192, 512):                                     # only 128- and 256-byte rows
+        assert lib.pa_probe_gather(fake, fake, 16, 8, row, 64, 2048, fake, None) != 0
+    assert lib.pa_probe_gather(fake, fake, 16, 1 << 20, 256, 64, 2048, fake, None) != 0   # block over 1 GiB
+    assert lib.pa_probe_gather(None, fake, 16, 8, 128, 64, 2048, fake, None) != 0
