@@ -101,21 +101,17 @@ def measured_traffic(workload):
     return int(fields["traffic_bytes_per_call"]) if h.hexdigest() == fields["kernel_sources_sha256"] else None
 
 
-def time_workload(name, steps, warmup, replicas, snapshot=False, partition_size=None, use_graphs=False, window=0,
+def time_workload(name, steps, warmup, replicas, sample=None, partition_size=None, use_graphs=False, window=0,
                   q_len=1, shared_prefix=False):
     import torch
     import paged_kv_cache_187_amd as pa
     import synth
-    from synth import bits_np
 
     overrides = {} if partition_size is None else {"partition_size": partition_size}
     w = synth.make_workload(name, device="cuda", **overrides)
     cfg = w.cfg
-    host = None
-    if snapshot:   # pre-step host copies for the CPU baseline
-        host = {"query": bits_np(w.query), "key_cache": bits_np(w.key_cache),
-                "value_cache": bits_np(w.value_cache), "key_new": bits_np(w.key_new),
-                "value_new": bits_np(w.value_new), "slot_mapping": w.slot_mapping.cpu().numpy()}
+    # pre-step host copies for the CPU baseline (sample = heads kept per sequence, 0 = all)
+    host = None if sample is None else cpu_sample(w, heads_per_seq=sample or None)
     kcs = [w.key_cache] + [w.key_cache.clone() for _ in range(replicas - 1)]
     vcs = [w.value_cache] + [w.value_cache.clone() for _ in range(replicas - 1)]
     kss = [w.k_scale] + [None if w.k_scale is None else w.k_scale.clone() for _ in range(replicas - 1)]
@@ -197,7 +193,7 @@ def time_workload(name, steps, warmup, replicas, snapshot=False, partition_size=
     n = len(dec_ms)
     return {
         "w": w,
-        "host": host,
+        "cpu_sample": host,
         "ms_per_step": (t1 - t0) * 1e3 / steps,
         "decode_ms_mean": sum(dec_ms) / n,
         "decode_ms_p10": dec_ms[n // 10],
@@ -360,37 +356,162 @@ def time_swap(steps, warmup, pairs=256, num_blocks=1024):
     return res
 
 
-def cpu_baseline(w, host, min_seconds):
-    """The float64 oracle on the host, on the same workload (pre-step state), single-threaded."""
-    import numpy as np
-    from threadpoolctl import threadpool_limits
+# ---------------------------------------------------------------------------
+# CPU baseline: the float64 oracle, unchanged, on the host's cores.  A pool of worker
+# processes (one BLAS thread each) is started before anything touches the GPU; each worker
+# gets a share of a workload's sequences as compact host copies of their pre-step caches and
+# times whole oracle steps on them (the append of the sequence's new token, then the decode of
+# its rows).  Nothing the HIP path writes reaches the oracle.
 
+def _oracle_worker_init():
+    from threadpoolctl import threadpool_limits
+    global _BLAS_LIMIT
+    _BLAS_LIMIT = threadpool_limits(limits=1)   # kept alive: one BLAS thread per worker
+
+
+def _oracle_worker_ready(_):
+    import numpy as np  # noqa: F401
+    import oracle  # noqa: F401
+    return os.getpid()
+
+
+def _oracle_step_chunk(chunk, budget_s):
+    """Times oracle steps over ``chunk`` (a list of per-sequence samples) for about ``budget_s``.
+
+    Untimed set-up: an FP8 sample's cached tokens are first quantised into its compact pool by
+    the oracle's own quantising append.  Timed: repetitions of, for every sample, the append of
+    the new token followed by the decode of the sample's rows.  Returns (seconds, repetitions).
+    """
+    import numpy as np
     import oracle
 
+    prepared = []
+    for smp in chunk:
+        L, nblk = smp["L"], smp["nblk"]
+        if smp["cache_dtype"] == "fp8_e4m3":
+            hkv, d = smp["kn"].shape[1:]
+            kc = np.full((nblk, 16, hkv, d), 0x7F, dtype=np.uint8)
+            ks = np.full((nblk, 16), np.nan, dtype=np.float32)
+            kc, vc, ks, vs = oracle.append_kv_e4m3(kc, kc.copy(), ks, ks.copy(), smp["fill_k"], smp["fill_v"],
+                                                   smp["src_dtype"], np.arange(L - 1, dtype=np.int64))
+            prepared.append((smp, kc, vc, ks, vs))
+        else:
+            prepared.append((smp, smp["kc"], smp["vc"], None, None))
+
+    def one_rep():
+        for smp, kc, vc, ks, vs in prepared:
+            L, nblk = smp["L"], smp["nblk"]
+            slot = np.array([L - 1], dtype=np.int64)
+            if ks is not None:
+                k2, v2, ks2, vs2 = oracle.append_kv_e4m3(kc, vc, ks, vs, smp["kn"], smp["vn"], smp["src_dtype"], slot)
+            else:
+                (k2, v2), ks2, vs2 = oracle.append_kv(kc, vc, smp["kn"], smp["vn"], slot), None, None
+            out = oracle.paged_decode(smp["q"][None], k2, v2, np.arange(nblk)[None, :], np.array([L]), smp["scale"],
+                                      smp["q_dtype"], smp["cache_dtype"], ks2, vs2)
+            assert np.all(np.isfinite(out))
+
+    t0 = time.perf_counter()
+    one_rep()
+    t1 = time.perf_counter() - t0
+    reps = 1 + max(0, min(10000, int(budget_s / max(t1, 1e-6)) - 1))
+    for _ in range(reps - 1):
+        one_rep()
+    return time.perf_counter() - t0, reps
+
+
+def start_oracle_pool():
+    """Worker processes for the CPU baseline, started (spawn) before the GPU is touched, so that no
+    process is ever started from one that has initialised the GPU.  Sized to the host cores this
+    process may run on, at most 16 (one GPU's share of a host)."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    cores = len(os.sched_getaffinity(0))
+    workers = max(1, min(16, cores))
+    pool = cf.ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("spawn"),
+                                  initializer=_oracle_worker_init)
+    pids = set(pool.map(_oracle_worker_ready, range(4 * workers)))
+    return pool, workers, cores, len(pids)
+
+
+def cpu_sample(w, heads_per_seq=None, seed=0):
+    """Host copies of what the oracle needs for each sequence of workload ``w``, taken before the
+    step's append: the sequence's blocks (compact, in logical order), its queries, its new token,
+    and for an FP8 cache the source values of its cached tokens.  ``heads_per_seq``: keep only
+    that many seeded query heads (and their KV heads) per sequence (16-bit caches)."""
+    import numpy as np
+    import torch
+    from synth import bits_np
     cfg = w.cfg
-    q = host["query"]
-    kc0, vc0 = host["key_cache"], host["value_cache"]
-    kn, vn, slots = host["key_new"], host["value_new"], host["slot_mapping"]
-    reps = 0
-    with threadpool_limits(limits=1):
+    g = cfg.num_heads // cfg.num_kv_heads
+    rng = np.random.default_rng(seed)
+    fp8 = cfg.cache_dtype == "fp8_e4m3"
+    fill_row = {}
+    if fp8:
+        fill_row = {int(s): i for i, s in enumerate(w.fill_slots.cpu().tolist())}
+        fk, fv = w.fill_key.cpu(), w.fill_value.cpu()
+    q_all = w.query.cpu()
+    kn_all, vn_all = w.key_new.cpu(), w.value_new.cpu()
+    samples = []
+    for b in range(cfg.num_seqs):
+        L = int(w.lens_np[b])
+        if L == 0:
+            continue
+        nblk = (L + 15) // 16
+        if heads_per_seq is None:
+            heads = list(range(cfg.num_heads))
+            kv = list(range(cfg.num_kv_heads))
+        else:
+            assert not fp8 and g == 1, "head sampling is for MHA 16-bit caches"
+            heads = sorted(int(h) for h in rng.choice(cfg.num_heads, size=heads_per_seq, replace=False))
+            kv = heads
+        smp = {"L": L, "nblk": nblk, "scale": cfg.scale, "q_dtype": cfg.q_dtype, "cache_dtype": cfg.cache_dtype,
+               "src_dtype": cfg.src_dtype, "heads": len(heads), "all_heads": cfg.num_heads,
+               "q": bits_np(q_all[b, heads]), "kn": bits_np(kn_all[b:b + 1, kv]), "vn": bits_np(vn_all[b:b + 1, kv])}
+        if fp8:
+            rows = [fill_row[int(w.tables_np[b][t // 16]) * 16 + t % 16] for t in range(L - 1)]
+            idx = torch.tensor(rows, dtype=torch.int64)
+            smp["fill_k"], smp["fill_v"] = bits_np(fk.index_select(0, idx)), bits_np(fv.index_select(0, idx))
+        else:
+            ids = torch.from_numpy(w.tables_np[b, :nblk].astype(np.int64)).to(w.key_cache.device)
+            kvi = torch.tensor(kv, dtype=torch.int64, device=w.key_cache.device)
+            smp["kc"] = bits_np(w.key_cache.index_select(0, ids).index_select(2, kvi))
+            smp["vc"] = bits_np(w.value_cache.index_select(0, ids).index_select(2, kvi))
+        eb = 1 if fp8 else 2
+        smp["bytes"] = (L * len(kv) * cfg.head_dim * 2 * eb + (8 * L if fp8 else 0) + len(heads) * cfg.head_dim * 2
+                        + nblk * 4 + 4)
+        samples.append(smp)
+    return samples
+
+
+def cpu_baseline(pool, workers, cores, samples_by_config, seconds):
+    """The oracle's rate on the host cores for every workload's sample (about ``seconds`` of work per
+    workload on every worker).  tokens/s counts decoded sequence steps (a sample holding h of a
+    sequence's H heads counts h / H of a step); GB/s is the algorithmic bytes the oracle's
+    decodes cover, per second."""
+    out = {}
+    for name, samples in samples_by_config.items():
+        order = sorted(samples, key=lambda s: -s["L"] * s["heads"])
+        chunks = [order[i::workers] for i in range(workers)]
+        chunks = [c for c in chunks if c]
         t0 = time.perf_counter()
-        while True:
-            kc, vc = oracle.append_kv(kc0, vc0, kn, vn, slots)
-            out = oracle.paged_decode(q, kc, vc, w.tables_np, w.lens_np, cfg.scale, cfg.q_dtype, cfg.cache_dtype)
-            reps += 1
-            el = time.perf_counter() - t0
-            if el >= min_seconds:
-                break
-    assert np.all(np.isfinite(out))
-    return {
-        "value": round(cfg.num_seqs * reps / el, 3),
-        "unit": "tokens/s",
-        "cores": 1,
-        "kind": "oracle",
-        "sample": f"{reps} full step(s) of the {cfg.name} workload (append of {cfg.num_seqs} tokens + float64 "
-                  f"decode of all {cfg.num_seqs}x{cfg.num_heads} (sequence, head) pairs) in {el:.1f} s, "
-                  f"numpy/BLAS limited to 1 thread",
-    }
+        res = list(pool.map(_oracle_step_chunk, chunks, [seconds] * len(chunks)))
+        wall = time.perf_counter() - t0
+        tok_rate = sum(sum(s["heads"] / s["all_heads"] for s in c) * reps / el for c, (el, reps) in zip(chunks, res))
+        byte_rate = sum(sum(s["bytes"] for s in c) * reps / el for c, (el, reps) in zip(chunks, res))
+        per_worker = [sum(s["heads"] / s["all_heads"] for s in c) * reps / el for c, (el, reps) in zip(chunks, res)]
+        rows = sum(s["heads"] for s in samples)
+        out[name] = {"tokens_per_s": round(tok_rate, 3), "GBs": round(byte_rate / 1e9, 4),
+                     "cores": len(chunks), "wall_s": round(wall, 1),
+                     "per_core_tokens_per_s": round(sum(per_worker) / len(per_worker), 3),
+                     "sample": f"{len(samples)} sequence(s), {rows} (sequence, head) row(s) of "
+                               f"{samples[0]['all_heads']} head(s) each, split over {len(chunks)} worker process(es), "
+                               f"each repeating its share's append + float64 decode for ~{seconds:g} s"}
+    return out
+
+
+# Heads per sequence in the CPU baseline's sample (0 or absent: every head).  The long-context
+# workload's caches are 10.7 GB, so its sample is 2 seeded heads of each of its 8 sequences.
+CPU_SAMPLE_HEADS = {"longctx": 2}
 
 
 def summarize(name, r):
@@ -431,7 +552,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=3, help="pool replicas rotated across steps")
     ap.add_argument("--also", default="gqa70b,fp8beams,longctx", help="comma-separated extra workloads reported alongside "
                     "(a workload with shared-prefix beams is also timed through pa_decode_shared_prefix)")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time for cpu_baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=4.0,
+                    help="oracle time per workload and worker for cpu_baseline (seconds)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graphs", action="store_true", help="replay captured HIP graphs of each replica's append "
                     "and decode instead of launching from Python (slower on ROCm 7 for this two-launch step)")
@@ -454,6 +576,9 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    # The oracle's worker processes start before anything touches the GPU.
+    oracle_pool = None if (args.no_cpu_baseline or args.calibrate_copy) else start_oracle_pool()
+
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -475,15 +600,26 @@ def main():
     if args.shared_prefix and synth.CONFIGS[args.workload].beams < 2:
         print(f"--shared-prefix needs a workload with shared-prefix beams, not {args.workload}", file=sys.stderr)
         sys.exit(2)
-    main_r = time_workload(args.workload, args.steps, args.warmup, args.replicas,
-                           snapshot=not args.no_cpu_baseline, partition_size=args.partition_size,
-                           use_graphs=args.graphs, shared_prefix=args.shared_prefix)
+    def sample_of(name):
+        """Heads kept per sequence in the CPU baseline's sample (0 = all), None without a baseline."""
+        if oracle_pool is None:
+            return None
+        return CPU_SAMPLE_HEADS.get(name, 0)
+
+    cpu_samples = {}
+    main_r = time_workload(args.workload, args.steps, args.warmup, args.replicas, sample=sample_of(args.workload),
+                           partition_size=args.partition_size, use_graphs=args.graphs,
+                           shared_prefix=args.shared_prefix)
     s = summarize(args.workload, main_r)
     cfg = main_r["w"].cfg
+    if oracle_pool is not None:
+        cpu_samples[args.workload] = main_r["cpu_sample"]
     also = {}
     for name in [n for n in args.also.split(",") if n and n != args.workload]:
-        r = time_workload(name, args.steps, args.warmup, args.replicas, partition_size=args.partition_size,
-                          use_graphs=args.graphs)
+        r = time_workload(name, args.steps, args.warmup, args.replicas, sample=sample_of(name),
+                          partition_size=args.partition_size, use_graphs=args.graphs)
+        if oracle_pool is not None:
+            cpu_samples[name] = r["cpu_sample"]
         also[name] = summarize(name, r)
         also[name]["traffic"] = measured_traffic(name)
         del r
@@ -555,8 +691,19 @@ def main():
         # achievable read bandwidth on this machine (probe kernels), labelled apart from the decode
         "ceiling": ceiling,
     }
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(main_r["w"], main_r["host"], args.cpu_seconds)
+    if oracle_pool is not None:
+        pool, workers, host_cores, started = oracle_pool
+        if "tiny" not in cpu_samples:
+            cpu_samples["tiny"] = cpu_sample(synth.make_workload("tiny"))
+        by_cfg = cpu_baseline(pool, workers, host_cores, cpu_samples, args.cpu_seconds)
+        pool.shutdown()
+        main_cpu = by_cfg[args.workload]
+        result["cpu_baseline"] = {
+            "value": main_cpu["tokens_per_s"], "unit": "tokens/s", "cores": main_cpu["cores"], "kind": "oracle",
+            "sample": f"{args.workload}: {main_cpu['sample']}",
+            "host_cores": host_cores, "worker_processes": started, "blas_threads_per_worker": 1,
+            "by_config": by_cfg,
+        }
     print(json.dumps(result), flush=True)
 
 

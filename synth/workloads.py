@@ -178,7 +178,7 @@ def build_tables(cfg, lens, rng):
         for n in lens:
             rows.append(pool.allocate_tokens(int(n)))
     max_blocks = max(1, max(len(r) for r in rows))
-    free = np.array(list(pool.free), dtype=np.int64)
+    free = np.array(pool.free_ids(), dtype=np.int64)
     tables = np.zeros((B, max_blocks), dtype=np.int32)
     for b, r in enumerate(rows):
         tables[b, :len(r)] = r

@@ -89,26 +89,30 @@ def assert_close(out_gpu, ref, cache_dtype, what=""):
     return max_abs, rel
 
 
-def sampled_reference(wh_tables, wh_lens, query_host, kc_dev, vc_dev, key_new, value_new, slot_mapping, cfg,
-                      pairs, ks_dev=None, vs_dev=None):
-    """Oracle outputs for a few (sequence, head) pairs of a workload too large to copy to the host.
+def sequence_reference(cfg, tables_np, lens_np, query_host, kc_dev, vc_dev, key_new, value_new, seqs):
+    """Oracle rows (all query heads) of sequences ``seqs`` of a 16-bit-cache workload too large to copy
+    to the host whole.
 
-    Only the blocks of the sampled sequences and their KV head are copied (before the HIP
-    step runs); the oracle applies this step's append to its compact copy itself.
+    Call it before the HIP step runs: only the blocks of one sequence at a time are copied (all KV
+    heads, pre-step contents), the oracle applies this step's append to that compact copy itself
+    (the new token of a sequence of length L sits at compact slot L - 1) and decodes every head.
+    Returns {b: float64 [Hq, D]}.  FP8 caches are filled by the append itself, so they have no
+    pre-step contents to copy: this helper refuses them.
     """
+    assert cfg.cache_dtype in ("f16", "bf16"), "sequence_reference covers 16-bit caches"
     refs = {}
-    g = cfg.num_heads // cfg.num_kv_heads
-    for b, h in pairs:
-        L = int(wh_lens[b])
+    for b in seqs:
+        L = int(lens_np[b])
         nblk = synth.blocks_for(L)
-        ids = torch.from_numpy(wh_tables[b, :nblk].astype(np.int64)).to(kc_dev.device)
-        hk = h // g
-        kc = bits_np(kc_dev.index_select(0, ids)[:, :, hk:hk + 1, :])
-        vc = bits_np(vc_dev.index_select(0, ids)[:, :, hk:hk + 1, :])
-        compact_slot = np.array([((L - 1) // 16) * 16 + (L - 1) % 16], dtype=np.int64)
-        kc, vc = oracle.append_kv(kc, vc, bits_np(key_new[b:b + 1, hk:hk + 1]), bits_np(value_new[b:b + 1, hk:hk + 1]),
-                                  compact_slot)
-        q = oracle.decode_bits(bits_np(query_host[b, h]), cfg.q_dtype)
-        refs[(b, h)] = oracle.paged_decode_one(q, kc, vc, np.arange(nblk), L, 0, cfg.scale, cfg.cache_dtype)
-    del slot_mapping
+        if L == 0:
+            refs[b] = np.zeros((cfg.num_heads, cfg.head_dim))
+            continue
+        ids = torch.from_numpy(tables_np[b, :nblk].astype(np.int64)).to(kc_dev.device)
+        kc = bits_np(kc_dev.index_select(0, ids))
+        vc = bits_np(vc_dev.index_select(0, ids))
+        kc, vc = oracle.append_kv(kc, vc, bits_np(key_new[b:b + 1]), bits_np(value_new[b:b + 1]),
+                                  np.array([L - 1], dtype=np.int64))
+        refs[b] = oracle.paged_decode(bits_np(query_host[b:b + 1]), kc, vc, np.arange(nblk)[None, :],
+                                      np.array([L]), cfg.scale, cfg.q_dtype, cfg.cache_dtype)[0]
+        del kc, vc
     return refs

@@ -104,3 +104,4 @@ def test_quantiser_every_representable_source_value(src):
     assert np.array_equal(bits_np(kcd), ek)
     assert np.array_equal(bits_np(vcd), ev)
     assert np.array_equal(ksd.cpu().numpy().view(np.uint32), eks.view(np.uint32))
+    assert np.array_equal(vsd.cpu().numpy().view(np.uint32), evs.view(np.uint32))

@@ -8,8 +8,8 @@ import oracle
 import paged_kv_cache_187_amd as pa
 import synth
 
-from gpu_cases import (assert_close, gpu_decode, gpu_step, oracle_caches, oracle_decode, sampled_reference,
-                       to_device)
+from gpu_cases import (assert_close, gpu_append, gpu_decode, gpu_step, oracle_caches, oracle_decode,
+                       sequence_reference, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -164,19 +164,51 @@ def test_full_size_config(name):
     _run_and_check(cfg, what=f"{name} full")
 
 
-def test_long_context_sampled():
-    _say("longctx (sampled pairs)")
+@pytest.mark.parametrize("half", [0, 1])
+def test_long_context_every_row(half):
+    """The long-context workload at full size (lengths 32K-128K, 512-token partitions merged by the
+    long-list merge): every (sequence, head) row of one half of the batch against the oracle, so the
+    two cases together check all 8 x 32 rows."""
     cfg = synth.CONFIGS["longctx"]
+    seqs = list(range(half * cfg.num_seqs // 2, (half + 1) * cfg.num_seqs // 2))
+    _say(f"longctx every row of sequences {seqs}")
     w = synth.make_workload(cfg, device="cuda")
-    rng = np.random.default_rng(0)
-    pairs = [(b, int(rng.integers(cfg.num_heads))) for b in range(cfg.num_seqs)]
-    q_host = w.query.cpu()
-    refs = sampled_reference(w.tables_np, w.lens_np, q_host, w.key_cache, w.value_cache, w.key_new.cpu(),
-                             w.value_new.cpu(), None, cfg, pairs)
+    refs = sequence_reference(cfg, w.tables_np, w.lens_np, w.query.cpu(), w.key_cache, w.value_cache,
+                              w.key_new.cpu(), w.value_new.cpu(), seqs)
     out = gpu_step(w)
     got = out.cpu()
-    for (b, h), ref in refs.items():
-        assert_close(got[b, h], ref, cfg.cache_dtype, f"longctx b={b} h={h} L={w.lens_np[b]}")
+    for b in seqs:
+        assert_close(got[b], refs[b], cfg.cache_dtype, f"longctx b={b} L={w.lens_np[b]} (all heads)")
+
+
+@pytest.mark.parametrize("hq,hkv,part", [(4, 4, 0), (16, 2, 0), (4, 4, 32), (16, 2, 64)])
+def test_context_lens_clamped_to_the_stated_bounds(hq, hkv, part):
+    """Lengths above max_context_len, or above what the page table can hold (16 x its columns), are
+    read as the bound; negative lengths as 0 (a zero row).  Compared with the oracle on the clamped
+    lengths."""
+    _say(f"clamped lengths Hq={hq} Hkv={hkv} part={part}")
+    lens = (300, 47, 129, 5, 200, 64)
+    cfg = _cfg(name="clamp", num_seqs=len(lens), num_heads=hq, num_kv_heads=hkv, len_args=lens, seed=21,
+               partition_size=part)
+    wh = synth.make_workload(cfg)
+    w = to_device(wh)
+    gpu_append(w)
+    caches = oracle_caches(wh)
+    for cap, cols in ((100, None), (1000, 5)):
+        tables = w.block_tables if cols is None else w.block_tables[:, :cols].contiguous()
+        bound = cap if cols is None else min(cap, 16 * cols)
+        ctx = w.context_lens.clone()
+        ctx[3] = -7                                  # negative: an empty sequence
+        out = torch.empty_like(w.query)
+        pa.pa_decode(out, w.query, w.key_cache, w.value_cache, tables, ctx, cfg.scale, cap, partition_size=part)
+        torch.cuda.synchronize()
+        eff = np.clip(ctx.cpu().numpy(), 0, bound)
+        assert (eff < wh.lens_np).any()
+        kc, vc, _, _ = caches
+        ref = oracle.paged_decode(synth.bits_np(wh.query), kc, vc, wh.tables_np, eff, cfg.scale, cfg.q_dtype,
+                                  cfg.cache_dtype)
+        assert_close(out, ref, cfg.cache_dtype, f"clamp cap={cap} cols={cols}")
+        assert torch.count_nonzero(out[3]) == 0
 
 
 def test_balanced_split_more_than_64_sequences():

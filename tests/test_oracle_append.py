@@ -1,6 +1,7 @@
 """Pins of the oracle's slot-mapped append and its per-token FP8 quantiser."""
 
 import numpy as np
+import pytest
 import torch
 
 import oracle
@@ -42,7 +43,6 @@ def test_append_matches_elementwise_loop_and_leaves_other_slots():
 
 
 def test_quantiser_amax_maps_to_448_and_error_within_half_ulp():
-    rng = np.random.default_rng(1)
     x_bf16 = torch.randn(64, 1024, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
     x = x_bf16.to(torch.float32).numpy()
     codes, scales = oracle.quantize_tokens_e4m3(x)
@@ -59,7 +59,6 @@ def test_quantiser_amax_maps_to_448_and_error_within_half_ulp():
     half_ulp = 0.5 * 2.0 ** (e - 3)
     bound = (half_ulp + y * 2.0 ** -24) * scales[:, None]
     assert np.all(np.abs(deq - x) <= bound + 1e-30)
-    del rng
 
 
 def test_quantiser_zero_row_and_signs():
@@ -84,27 +83,53 @@ def test_quantiser_agrees_with_torch_conversion_of_the_scaled_values():
     assert np.array_equal(codes, ref)
 
 
-def test_fp8_append_scatter_writes_codes_and_scales():
-    rng = np.random.default_rng(5)
-    nb, hkv, d, T = 4, 2, 16, 5
+def _torch_quantise(x):
+    """Per-token E4M3 codes and scales computed with torch alone (not the oracle's encoder):
+    amax and the float32 division by 448 in torch, then torch's own E4M3 conversion of the
+    float32 quotients, clamped to +-448 first (torch's conversion gives NaN past 464)."""
+    x = x.to(torch.float32)
+    amax = x.abs().amax(dim=1)
+    sc = torch.where(amax == 0, torch.ones_like(amax), amax / torch.tensor(448.0))
+    y = (x / sc[:, None]).clamp(-448, 448)
+    return y.to(torch.float8_e4m3fn).view(torch.uint8).numpy(), sc.numpy()
+
+
+@pytest.mark.parametrize("src", ["bf16", "f16"])
+def test_fp8_append_scatter_writes_codes_and_scales(src):
+    """Both halves of the quantising append: K codes and scales from K, V codes and scales from
+    V (drawn apart so that a swapped operand fails), every other slot and scale unchanged,
+    slots past the pool (16 * num_blocks and above) and negative slots skipped."""
+    nb, hkv, d, T = 4, 2, 16, 7
+    tdt = torch.bfloat16 if src == "bf16" else torch.float16
     kc = np.full((nb, BS, hkv, d), 0x7F, dtype=np.uint8)
-    vc = kc.copy()
+    vc = np.full((nb, BS, hkv, d), 0x7F, dtype=np.uint8)
     ks = np.full((nb, BS), np.nan, dtype=np.float32)
-    vs = ks.copy()
-    k = torch.randn(T, hkv, d, generator=torch.Generator().manual_seed(1)).to(torch.bfloat16)
-    v = torch.randn(T, hkv, d, generator=torch.Generator().manual_seed(2)).to(torch.bfloat16)
+    vs = np.full((nb, BS), np.nan, dtype=np.float32)
+    k = torch.randn(T, hkv, d, generator=torch.Generator().manual_seed(1)).to(tdt)
+    v = (torch.randn(T, hkv, d, generator=torch.Generator().manual_seed(2)) * 5).to(tdt)
+    v[2] = 0                                          # an all-zero V row: scale 1, codes 0
     kb = k.view(torch.int16).numpy().view(np.uint16)
     vb = v.view(torch.int16).numpy().view(np.uint16)
-    slots = np.array([3, -1, 17, 63, 32], dtype=np.int64)
-    nk, nv, nks, nvs = oracle.append_kv_e4m3(kc, vc, ks, vs, kb, vb, "bf16", slots)
-    qk, sk = oracle.quantize_tokens_e4m3(k.to(torch.float32).numpy().reshape(T, -1))
+    slots = np.array([3, -1, 17, 63, 32, nb * BS, nb * BS + 5], dtype=np.int64)
+    nk, nv, nks, nvs = oracle.append_kv_e4m3(kc, vc, ks, vs, kb, vb, src, slots)
+    qk, sk = _torch_quantise(k.reshape(T, -1))
+    qv, sv = _torch_quantise(v.reshape(T, -1))
+    assert not np.array_equal(qk, qv) and not np.array_equal(sk, sv)
+    assert sv[2] == 1.0 and np.all(qv[2] == 0)
+    written = np.zeros((nb, BS), dtype=bool)
     for t, s in enumerate(slots):
-        if s < 0:
+        if s < 0 or s >= nb * BS:
             continue
-        assert np.array_equal(nk[s // BS, s % BS].reshape(-1), qk[t])
-        assert nks[s // BS, s % BS] == sk[t]
-    untouched = np.ones((nb, BS), dtype=bool)
-    for s in slots[slots >= 0]:
-        untouched[s // BS, s % BS] = False
-    assert np.all(nk[untouched] == 0x7F) and np.all(np.isnan(nks[untouched]))
-    assert rng is not None
+        blk, off = divmod(int(s), BS)
+        written[blk, off] = True
+        assert np.array_equal(nk[blk, off].reshape(-1), qk[t]), f"K codes of token {t}"
+        assert np.array_equal(nv[blk, off].reshape(-1), qv[t]), f"V codes of token {t}"
+        assert nks[blk, off].view(np.uint32) == sk[t].view(np.uint32), f"K scale of token {t}"
+        assert nvs[blk, off].view(np.uint32) == sv[t].view(np.uint32), f"V scale of token {t}"
+    assert written.sum() == 4
+    for pool in (nk, nv):
+        assert np.all(pool[~written] == 0x7F)
+    for sc in (nks, nvs):
+        assert np.all(np.isnan(sc[~written]))
+    # the arguments are left as they were
+    assert np.all(kc == 0x7F) and np.all(vc == 0x7F) and np.isnan(ks).all() and np.isnan(vs).all()

@@ -12,20 +12,26 @@ def test_blocks_for_is_ceiling_of_tokens_over_16():
     assert [blocks_for(n) for n in (0, 1, 15, 16, 17, 32, 33)] == [0, 1, 1, 1, 2, 2, 3]
 
 
-def test_pool_fifo_exhaustion_and_refcounts():
+def test_pool_order_exhaustion_and_refcounts():
     pool = BlockPool([5, 3, 9, 1])
-    a = pool.allocate_tokens(17)          # 2 blocks from the front
+    a = pool.allocate_tokens(17)          # ceil(17 / 16) = 2 blocks, in the given order
     assert a == [5, 3]
     with pytest.raises(PoolExhausted):
         pool.allocate(3)
+    assert pool.free_ids() == [9, 1]       # a failed request takes nothing
     pool.share(a)                          # a second holder
     pool.release(a)
-    assert list(pool.free) == [9, 1]       # still held once
+    assert pool.free_ids() == [9, 1]       # still held once
+    assert pool.utilization() == 0.5
     pool.release(a)
-    assert list(pool.free) == [9, 1, 5, 3]  # returned to the back, in order
+    assert pool.free_ids() == [9, 1, 5, 3]  # given back after the never-used ids, in order
     assert pool.utilization() == 0.0
     with pytest.raises(ValueError):
         pool.release([5])
+    with pytest.raises(ValueError):
+        pool.share([9])
+    assert pool.allocate(3) == [9, 1, 5]    # never-used ids first, then returned ones
+    assert pool.allocate_tokens(0) == []
 
 
 def test_slot_of():
