@@ -31,6 +31,7 @@ struct Plan {
     bool mfma;           // matrix-core path
     int64_t groups;      // head groups per sequence
     int64_t waves;       // waves in the grid
+    int64_t teams;       // balanced split: teams of `groups` waves (one per head group)
     int64_t slots;       // workspace slots (each HPW heads x (D + 2) floats)
 };
 
@@ -62,10 +63,16 @@ Plan make_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_
     if (seq_groups * (max_blocks > 0 ? max_blocks : 1) >= kMaxWork) return pl;
     pl.balanced = partition_size == 0;
     if (pl.balanced) {
-        const int64_t work = seq_groups * max_blocks;   // upper bound of (head group, block) pairs
-        pl.waves = work < kBalancedWaves ? (work > 0 ? work : 1) : kBalancedWaves;
-        // a partial goes to slot range + (sequence, head group)
-        pl.slots = pl.waves + seq_groups;
+        // Teams of one wave per head group share a range of (sequence, block) positions:
+        // about kBalancedWaves waves, at most one team per block and at least one team.
+        const int64_t blocks = entries * max_blocks;   // upper bound of (entry, block) positions
+        int64_t teams = kBalancedWaves / pl.groups;
+        if (teams > blocks) teams = blocks;
+        if (teams < 1) teams = 1;
+        pl.teams = teams;
+        pl.waves = teams * pl.groups;
+        // a partial goes to slot hg * (teams + entries) + range + entry
+        pl.slots = pl.groups * (teams + entries);
     } else {
         pl.part = partition_size;
         pl.np = (max_context_len + partition_size - 1) / partition_size;
@@ -188,6 +195,7 @@ pa_status decode_impl(void* out, const void* query, const void* key_cache, const
     p.rows = (int32_t)(pl.qpw * pl.hpw);
     p.mfma = pl.mfma ? 1 : 0;
     p.num_waves = (int32_t)pl.waves;
+    p.teams = (int32_t)pl.teams;
     p.window = window;
     p.scale_log2 = scale * 1.4426950408889634f;
     p.sgroup = seq_group;

@@ -13,12 +13,16 @@
 // Work split.  Every wave works alone (no barriers; the matrix-core path uses a
 // per-wave LDS tile) on segments: runs of consecutive 16-token blocks of one
 // (sequence, head group), a head group being the query heads of one KV head
-// that one wave serves.  Two ways to cut the work:
-//  * fixed partitions: wave = (sequence, head group, partition of P tokens);
-//  * balanced: the (sequence, head group, block) space is laid end to end and
-//    cut into equal ranges, one per wave, so long and short sequences cost
-//    the same per wave; a range may cover the end of one sequence and the
-//    start of the next.
+// that one wave serves.  The waves come in teams of one wave per head group:
+// the waves of a team read the same blocks at about the same time, each its
+// own head's rows, so every block is fetched whole (all heads) within a short
+// window, which the memory system serves faster than the same rows spread
+// over the kernel's whole run.  Two ways to cut the work:
+//  * fixed partitions: team = (sequence, partition of P tokens);
+//  * balanced: the (sequence, block) positions are laid end to end and cut
+//    into equal ranges, one per team, so long and short sequences cost the
+//    same per wave; a range may cover the end of one sequence and the start
+//    of the next.
 // A segment that covers its whole sequence writes the output row; otherwise
 // it writes a partial result (running max m, sum of exponentials l,
 // unnormalised V sum) that decode_merge_kernel combines in ascending token
@@ -149,11 +153,11 @@ __device__ SeqTable seq_table(const DecodeParams& p, int lane) {
     return st;
 }
 
-// The non-empty entry holding balanced-order position pos, where the position of
-// (b, hg, j) is groups * start_b + hg * nblk_b + j and 0 <= pos < groups * total_blocks.
+// The non-empty entry holding balanced-order position pos, where the position of block j
+// of entry b is start_b + j and 0 <= pos < total_blocks.
 __device__ SeqPos locate(const DecodeParams& p, const SeqTable& st, int lane, int pos) {
     if (st.single) {
-        const uint64_t mask = __ballot(st.nb > 0 && p.groups * st.start <= pos);
+        const uint64_t mask = __ballot(st.nb > 0 && st.start <= pos);
         const int lb = 63 - __builtin_clzll(mask);
         return {lb, __builtin_amdgcn_readlane(st.start, lb), __builtin_amdgcn_readlane(st.nb, lb)};
     }
@@ -164,9 +168,9 @@ __device__ SeqPos locate(const DecodeParams& p, const SeqTable& st, int lane, in
         const int nb = b < n ? entry_blocks(p, b) : 0;
         const int incl = wave_incl_scan(nb, lane);
         const int start = carry + incl - nb;
-        const uint64_t mask = __ballot(nb > 0 && p.groups * start <= pos);
+        const uint64_t mask = __ballot(nb > 0 && start <= pos);
         const int chunk_total = __builtin_amdgcn_readlane(incl, kWave - 1);
-        if (p.groups * (carry + chunk_total) > pos) {
+        if (carry + chunk_total > pos) {
             const int lb = 63 - __builtin_clzll(mask);
             return {c + lb, __builtin_amdgcn_readlane(start, lb), __builtin_amdgcn_readlane(nb, lb)};
         }
@@ -191,11 +195,13 @@ __device__ SeqPos seq_entry(const DecodeParams& p, const SeqTable& st, int lane,
     return {b, carry, 0};
 }
 
-// Ranges of the balanced split: the T positions are cut into W equal ranges of
-// C = ceil(T / W) positions, range w running on wave w.  Range boundaries depend
-// only on the lengths and the launch shape; a partial goes to slot
-// range + (sequence, head group), which is unique because ranges and sequences
-// both advance with the position.
+// Ranges of the balanced split: the T block positions are cut into `teams` equal ranges
+// of C = ceil(T / teams) positions, range r running on team r (waves r * groups ..
+// r * groups + groups - 1, one per head group).  Range boundaries depend only on the
+// lengths and the launch shape.  The partial of entry e, head group hg from range r goes
+// to workspace slot hg * (teams + entries) + r + e: for one head group, r + e is unique
+// because ranges and entries both advance with the position, and the slots of one
+// (entry, head group) are consecutive in r, i.e. in token order.
 struct Ranges {
     int T, C;
     __device__ int begin(int w) const { return min(T, w * C); }
@@ -210,7 +216,7 @@ constexpr int kMinGroupRange = 16;
 __device__ Ranges make_ranges(const DecodeParams& p, int T) {
     Ranges r;
     r.T = T;
-    r.C = T > 0 ? (T + p.num_waves - 1) / p.num_waves : 1;
+    r.C = T > 0 ? (T + p.teams - 1) / p.teams : 1;
     if (p.sgroup > 0 && r.C < kMinGroupRange) r.C = kMinGroupRange;
     return r;
 }
@@ -947,11 +953,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeParams p) 
     if (w >= p.num_waves) return;
 
     if (!p.balanced) {
-        // Fixed partitions: wave w = (partition, head group, sequence), partition fastest.
-        const int part = w % p.NP;
-        const int s = w / p.NP;
-        const int hg = s % p.groups;
-        const int b = s / p.groups;
+        // Fixed partitions: wave w = (head group, partition, sequence), head group fastest, so
+        // the waves of a team read one partition's blocks together.
+        const int hg = w % p.groups;
+        const int part = (w / p.groups) % p.NP;
+        const int b = w / (p.groups * p.NP);
+        const int s = b * p.groups + hg;
         // Partitions cover the blocks in play, j0 .. nblk - 1.
         const int L = seq_len(p, b);
         const int lo = first_token(p, L);
@@ -964,33 +971,35 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeParams p) 
         return;
     }
 
-    // Balanced split: range w of the (sequence, head group, block) order.
+    // Balanced split: head group hg of the range of team `team` in the (sequence, block) order.
+    const int team = w / p.groups;
+    const int hg = w % p.groups;
     const SeqTable st = seq_table(p, lane);
-    const Ranges rg = make_ranges(p, p.groups * st.total);
-    int pos = rg.begin(w);
-    const int pos_end = rg.end(w);
+    const Ranges rg = make_ranges(p, st.total);
+    int pos = rg.begin(team);
+    const int pos_end = rg.end(team);
+    const int64_t slot_base = (int64_t)hg * (p.teams + num_entries(p)) + team;
     int64_t deferred = -1;   // workspace slot of a stashed partial
     while (pos < pos_end) {
-        // Position offsets count the blocks in play of (sequence, head group), which start
-        // at logical block j0.
+        // Position offsets count the blocks in play of the sequence, which start at logical
+        // block j0.
         const SeqPos sp = locate(p, st, lane, pos);
-        const int off = pos - p.groups * sp.start;
-        const int hg = off / sp.nblk;
+        const int off = pos - sp.start;
         // entry sp.b: a sequence, or the group of sequences sp.b * sgroup .. (whose segment
         // resolves its own lengths)
         const int b = p.sgroup > 0 ? sp.b * p.sgroup : sp.b;
         const int L = p.sgroup > 0 ? 0 : seq_len(p, sp.b);
         const int lo = first_token(p, L);
         const int j0 = lo / kBlockSize;
-        const int jb = j0 + off % sp.nblk;
+        const int jb = j0 + off;
         const int je = min(j0 + sp.nblk, jb + (pos_end - pos));
-        const int s = sp.b * p.groups + hg;
+        const int64_t slot = slot_base + sp.b;
         // Only a wave's first segment can end unfinished before its last one; its partial
         // is written after the last segment (see the segment's stash).
         const bool last = pos + (je - jb) >= pos_end;
         const bool whole = jb == j0 && je == j0 + sp.nblk;
-        Segment::run(p, lane, b, hg, jb, je, j0, j0 + sp.nblk, lo, L, (int64_t)w + s, !last);
-        if (!last && !whole) deferred = (int64_t)w + s;
+        Segment::run(p, lane, b, hg, jb, je, j0, j0 + sp.nblk, lo, L, slot, !last);
+        if (!last && !whole) deferred = slot;
         pos += je - jb;
     }
     if (deferred >= 0) Segment::flush(p, lane, deferred);
@@ -1042,18 +1051,17 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodePara
         count = n_part;
     } else {
         const SeqTable st = seq_table(p, lane);
-        const Ranges rg = make_ranges(p, p.groups * st.total);
+        const Ranges rg = make_ranges(p, st.total);
         const SeqPos e = seq_entry(p, st, lane, ent);
         if (e.nblk == 0) {
 #pragma unroll
             for (int k = 0; k < EPT; ++k) orow[k * kWave + lane] = to_bits(QT{}, 0.0f);
             return;
         }
-        const int pos0 = p.groups * e.start + u * e.nblk;
-        const int t0 = rg.range_of(pos0);
-        const int t1 = rg.range_of(pos0 + e.nblk - 1);
+        const int t0 = rg.range_of(e.start);
+        const int t1 = rg.range_of(e.start + e.nblk - 1);
         if (t0 == t1) return;               // one segment: written directly
-        first = t0 + s;
+        first = (int64_t)u * (p.teams + num_entries(p)) + t0 + ent;
         count = t1 - t0 + 1;
     }
 

@@ -23,7 +23,7 @@ struct DecodeParams {
     float* ws_ml;              // [slots, HPW, 2] partial (max, sum of exponentials)
     int64_t num_blocks;
     int32_t B, Hq, Hkv, max_blocks, ctx_limit;  // ctx_limit = min(max_context_len, 16 * max_blocks)
-    int32_t balanced;          // 1: equal (sequence, head group, block) ranges per wave
+    int32_t balanced;          // 1: equal (sequence, block) ranges per team of `groups` waves
     int32_t NP;                // fixed split: partitions per sequence in the grid
     int32_t part_blocks;       // fixed split: partition length in 16-token blocks
     int32_t groups;            // work units per sequence = (Hq / hpw) head groups x qgroups query groups
@@ -34,6 +34,7 @@ struct DecodeParams {
     int32_t hpw;               // query heads per wave (all share one KV head)
     int32_t mfma;              // 1: matrix-core path (hpw <= 16 rows of a 16x16 tile)
     int32_t num_waves;         // waves in the grid
+    int32_t teams;             // balanced split: teams of `groups` waves, one range of blocks each
     int32_t window;            // sliding window in tokens (0: attend to the whole context)
     float scale_log2;          // softmax scale * log2(e)
     // Shared-prefix groups (matrix-core path, balanced split): sequences g*sgroup ..
