@@ -45,7 +45,8 @@
  * Ownership and ordering: every pointer argument is a caller-owned device
  * buffer (except where noted); the library allocates nothing, keeps nothing
  * after a call returns and has no mutable global state, so it may be called
- * from several threads.  Work is enqueued asynchronously on `stream` (a
+ * from several threads.  The one exception is pa_decode_noalloc, whose
+ * partial results live in a fixed device array per GPU (see there).  Work is enqueued asynchronously on `stream` (a
  * hipStream_t; NULL = the null stream); an append followed by a decode on
  * the same stream is ordered.  Host-side argument checks run before anything
  * is enqueued and never read device memory, so no call synchronises.
@@ -79,8 +80,13 @@ typedef enum pa_status {
     PA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required        */
     PA_ERR_HIP = 6,         /* the HIP runtime reported an error                 */
     PA_ERR_ALIGN = 7,       /* a buffer is not 16-byte aligned                   */
-    PA_ERR_ADDRESS = 8      /* a buffer is not addressable by the GPU            */
+    PA_ERR_ADDRESS = 8,     /* a buffer is not addressable by the GPU            */
+    PA_ERR_SCRATCH = 9      /* pa_decode_noalloc: the call needs more workspace
+                               than PA_NOALLOC_SCRATCH_BYTES                      */
 } pa_status;
+
+/* Size of the fixed device scratch behind pa_decode_noalloc (per GPU). */
+#define PA_NOALLOC_SCRATCH_BYTES (64u << 20)
 
 typedef enum pa_dtype {
     PA_F16 = 0,       /* IEEE binary16                                  */
@@ -234,6 +240,33 @@ pa_status pa_decode(void *out, const void *query,
                     int32_t q_dtype, int32_t cache_dtype,
                     void *workspace, size_t workspace_bytes,
                     void *stream);
+
+/*
+ * pa_decode_noalloc - pa_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Arguments, result, determinism and errors are those of pa_decode, without the
+ * workspace: the partial results live in a fixed device array of
+ * PA_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on until the
+ * process ends (resolved once per device, on the first call with that device current;
+ * `stream` must belong to the current device).  The call allocates nothing: no hipMalloc,
+ * no hipFree, no allocating library routine.  A call whose pa_decode_workspace_bytes(...)
+ * exceeds PA_NOALLOC_SCRATCH_BYTES returns PA_ERR_SCRATCH before anything is enqueued.
+ * All calls on one GPU share that GPU's array (it keeps the last call's partials; nothing
+ * in it needs to start at zero): calls that can overlap on one GPU (other streams, other
+ * threads) race and must be serialised by the caller; pa_decode with its own workspace
+ * has no such limit.  PA_ERR_HIP also reports a failure to resolve the array's address.
+ */
+pa_status pa_decode_noalloc(void *out, const void *query,
+                            const void *key_cache, const void *value_cache,
+                            const float *k_scale, const float *v_scale,
+                            const int32_t *block_tables, const int32_t *context_lens,
+                            int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int64_t num_blocks,
+                            int32_t max_blocks_per_seq, int32_t max_context_len,
+                            float scale, int32_t partition_size,
+                            int32_t q_dtype, int32_t cache_dtype,
+                            void *stream);
 
 /*
  * pa_decode_sliding - pa_decode with a sliding window: the query of a

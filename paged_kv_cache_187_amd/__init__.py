@@ -19,6 +19,7 @@ from .binding import (  # noqa: F401
     pa_copy_blocks,
     pa_decode,
     pa_decode_multi,
+    pa_decode_noalloc,
     pa_decode_shared_prefix,
     pa_decode_sliding,
     pa_swap_blocks,

@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 # Read-bandwidth probes (bench.py's ceiling line only; not part of the C ABI above).
 PROBE_SRC = os.path.join(PKG, "probe", "pa_probe.hip")
 PROBE_PATH = os.path.join(PKG, "libpaprobe.so")
-SOURCES = ["pa_append.hip", "pa_copy.hip", "pa_decode.hip", "pa_api.cpp"]
+SOURCES = ["pa_append.hip", "pa_copy.hip", "pa_decode.hip", "pa_scratch.hip", "pa_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 COMMON = [

@@ -140,7 +140,7 @@ pa_status decode_impl(void* out, const void* query, const void* key_cache, const
                     int32_t head_dim, int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
                     float scale, int32_t partition_size, int32_t q_dtype, int32_t cache_dtype, void* workspace,
                     size_t workspace_bytes, void* stream, int32_t window, int32_t q_len,
-                    int32_t seq_group = 0, const int32_t* prefix_blocks = nullptr) {
+                    int32_t seq_group = 0, const int32_t* prefix_blocks = nullptr, bool use_scratch = false) {
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 ||
         num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || num_heads > 65536)
         return PA_ERR_SHAPE;
@@ -153,16 +153,26 @@ pa_status decode_impl(void* out, const void* query, const void* key_cache, const
                               seq_group);
     if (!pl.ok) return PA_ERR_SHAPE;
     const size_t need = workspace_size(pl, head_dim);
+    if (use_scratch && need > PA_NOALLOC_SCRATCH_BYTES) return PA_ERR_SCRATCH;
     if (num_seqs == 0) return PA_OK;
     if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens) return PA_ERR_NULL;
     if (seq_group > 0 && !prefix_blocks) return PA_ERR_NULL;
     if (fp8 && (!k_scale || !v_scale)) return PA_ERR_NULL;
-    if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+    if (use_scratch) {
+        workspace = nullptr;
+        workspace_bytes = 0;
+    }
+    if (!use_scratch && need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
     if (!aligned(out, 16) || !aligned(query, 16) || !aligned(key_cache, 16) || !aligned(value_cache, 16) ||
         !aligned(block_tables, 4) || !aligned(context_lens, 4) || (need > 0 && !aligned(workspace, 16)) ||
         (seq_group > 0 && !aligned(prefix_blocks, 4)) ||
         (fp8 && (!aligned(k_scale, 16) || !aligned(v_scale, 16))))
         return PA_ERR_ALIGN;
+    if (use_scratch && need > 0) {
+        // every host check has passed: only now touch the device
+        if (pa::scratch_address(&workspace) != hipSuccess) return PA_ERR_HIP;
+        workspace_bytes = PA_NOALLOC_SCRATCH_BYTES;
+    }
 
     pa::DecodeParams p{};
     p.out = out;
@@ -218,6 +228,9 @@ const char* pa_status_string(int32_t status) {
         case PA_ERR_HIP: return "PA_ERR_HIP: the HIP runtime reported an error";
         case PA_ERR_ALIGN: return "PA_ERR_ALIGN: a buffer is not 16-byte aligned";
         case PA_ERR_ADDRESS: return "PA_ERR_ADDRESS: a buffer is not addressable by the GPU";
+        case PA_ERR_SCRATCH:
+            return "PA_ERR_SCRATCH: the call needs more workspace than the fixed scratch of pa_decode_noalloc "
+                   "(PA_NOALLOC_SCRATCH_BYTES); use pa_decode with a workspace";
         default: return "unknown pa_status";
     }
 }
@@ -310,6 +323,17 @@ pa_status pa_decode(void* out, const void* query, const void* key_cache, const v
     return decode_impl(out, query, key_cache, value_cache, k_scale, v_scale, block_tables, context_lens, num_seqs,
                        num_heads, num_kv_heads, head_dim, num_blocks, max_blocks_per_seq, max_context_len, scale,
                        partition_size, q_dtype, cache_dtype, workspace, workspace_bytes, stream, 0, 1);
+}
+
+pa_status pa_decode_noalloc(void* out, const void* query, const void* key_cache, const void* value_cache,
+                            const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                            const int32_t* context_lens, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int64_t num_blocks, int32_t max_blocks_per_seq,
+                            int32_t max_context_len, float scale, int32_t partition_size, int32_t q_dtype,
+                            int32_t cache_dtype, void* stream) {
+    return decode_impl(out, query, key_cache, value_cache, k_scale, v_scale, block_tables, context_lens, num_seqs,
+                       num_heads, num_kv_heads, head_dim, num_blocks, max_blocks_per_seq, max_context_len, scale,
+                       partition_size, q_dtype, cache_dtype, nullptr, 0, stream, 0, 1, 0, nullptr, true);
 }
 
 pa_status pa_decode_sliding(void* out, const void* query, const void* key_cache, const void* value_cache,

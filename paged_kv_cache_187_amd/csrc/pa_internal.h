@@ -72,4 +72,8 @@ HeadGrouping multi_query_grouping(int group);  // several queries per sequence
 
 hipError_t launch_decode(const DecodeParams& p, int head_dim, int q_kind, int cache_kind, hipStream_t stream);
 
+// Device address of the fixed decode scratch on the current device (resolved once per
+// device); used only by pa_decode_noalloc.
+hipError_t scratch_address(void** out);
+
 }  // namespace pa
