@@ -40,6 +40,8 @@ WORKLOAD_TEXT = {
     "fp8beams": "fp8-e4m3 KV with per-token scales, 16 prompts x 4 beams sharing 1024-token prefixes + 256 "
                 "private tokens, Hq=32, Hkv=8, D=128, Q bf16",
     "tiny": "tiny paged decode: B=4, lens {1,17,33,50}, Hq=Hkv=4, D=64, f16",
+    "llama7b_b256": "LLaMA-7B-shaped single-layer paged decode at B=256: Hq=Hkv=32, D=128, f16, context lens "
+                    "U[1,2048], pool +10%, permuted blocks",
 }
 
 
@@ -510,8 +512,9 @@ def cpu_baseline(pool, workers, cores, samples_by_config, seconds):
 
 
 # Heads per sequence in the CPU baseline's sample (0 or absent: every head).  The long-context
-# workload's caches are 10.7 GB, so its sample is 2 seeded heads of each of its 8 sequences.
-CPU_SAMPLE_HEADS = {"longctx": 2}
+# workload's caches are 10.7 GB, so its sample is 2 seeded heads of each of its 8 sequences;
+# the 256-sequence workload's 4.3 GB are sampled at 4 heads of each sequence.
+CPU_SAMPLE_HEADS = {"longctx": 2, "llama7b_b256": 4}
 
 
 def summarize(name, r):
@@ -550,7 +553,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama7b")
     ap.add_argument("--replicas", type=int, default=3, help="pool replicas rotated across steps")
-    ap.add_argument("--also", default="gqa70b,fp8beams,longctx", help="comma-separated extra workloads reported alongside "
+    ap.add_argument("--also", default="gqa70b,fp8beams,longctx,llama7b_b256", help="comma-separated extra workloads reported alongside "
                     "(a workload with shared-prefix beams is also timed through pa_decode_shared_prefix)")
     ap.add_argument("--cpu-seconds", type=float, default=4.0,
                     help="oracle time per workload and worker for cpu_baseline (seconds)")

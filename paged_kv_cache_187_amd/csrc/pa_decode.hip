@@ -195,18 +195,20 @@ __device__ SeqPos seq_entry(const DecodeParams& p, const SeqTable& st, int lane,
     return {b, carry, 0};
 }
 
-// Ranges of the balanced split: the T block positions are cut into `teams` equal ranges
-// of C = ceil(T / teams) positions, range r running on team r (waves r * groups ..
-// r * groups + groups - 1, one per head group).  Range boundaries depend only on the
-// lengths and the launch shape.  The partial of entry e, head group hg from range r goes
-// to workspace slot hg * (teams + entries) + r + e: for one head group, r + e is unique
-// because ranges and entries both advance with the position, and the slots of one
-// (entry, head group) are consecutive in r, i.e. in token order.
+// Ranges of the balanced split: the T block positions are cut into n <= teams ranges
+// whose lengths differ by at most one (range r is [floor(r T / n), floor((r + 1) T / n))),
+// range r running on team r (waves r * groups .. r * groups + groups - 1, one per head
+// group).  Range boundaries depend only on the lengths and the launch shape.  The partial
+// of entry e, head group hg from range r goes to workspace slot hg * (teams + entries) +
+// r + e: for one head group, r + e is unique because ranges and entries both advance with
+// the position, and the slots of one (entry, head group) are consecutive in r, i.e. in
+// token order.
 struct Ranges {
-    int T, C;
-    __device__ int begin(int w) const { return min(T, w * C); }
-    __device__ int end(int w) const { return min(T, (w + 1) * C); }
-    __device__ int range_of(int pos) const { return pos / C; }
+    int T, n;
+    __device__ int begin(int r) const { return r >= n ? T : (int)((int64_t)r * T / n); }
+    __device__ int end(int r) const { return begin(r + 1); }
+    // the r with begin(r) <= pos < end(r), for 0 <= pos < T
+    __device__ int range_of(int pos) const { return (int)((((int64_t)pos + 1) * n - 1) / T); }
 };
 
 // Shared-prefix groups write 16-row partials, so their ranges are at least this long
@@ -216,8 +218,9 @@ constexpr int kMinGroupRange = 16;
 __device__ Ranges make_ranges(const DecodeParams& p, int T) {
     Ranges r;
     r.T = T;
-    r.C = T > 0 ? (T + p.teams - 1) / p.teams : 1;
-    if (p.sgroup > 0 && r.C < kMinGroupRange) r.C = kMinGroupRange;
+    r.n = p.teams < T ? p.teams : T;        // no empty range: a unit's ranges are consecutive
+    if (p.sgroup > 0 && T / kMinGroupRange < r.n) r.n = T / kMinGroupRange;
+    if (r.n < 1) r.n = 1;
     return r;
 }
 

@@ -21,6 +21,7 @@ shared prefixes); sizes and distributions are fixed here:
             cache with per-token scales; each beam's table holds its prompt's
             1024-token prefix blocks (shared by the 4 beams) then 256 private
             tokens.
+* llama7b_b256  the llama7b shape with B=256 sequences.
 
 Conventions (all workloads):
 
@@ -85,6 +86,9 @@ CONFIGS = {
                             value_std=0.5, partition_size=512, seed=1004),
     "fp8beams": DecodeConfig("fp8beams", 64, 32, 8, 128, "bf16", "fp8_e4m3", "beams", (1280,),
                              seed=1005, beams=4, prefix_len=1024),
+    # the LLaMA-7B shape at a serving-size batch (the balanced split over more than 64 sequences)
+    "llama7b_b256": DecodeConfig("llama7b_b256", 256, 32, 32, 128, "f16", "f16", "uniform", (1, 2048),
+                                 seed=1006),
 }
 
 

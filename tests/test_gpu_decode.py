@@ -220,6 +220,21 @@ def test_balanced_split_more_than_64_sequences():
     _run_and_check(cfg, partition_size=0)
 
 
+@pytest.mark.parametrize("hq,hkv,D,part", [(2, 2, 64, 0), (8, 1, 64, 0), (4, 4, 128, 0), (8, 2, 64, 0),
+                                           (2, 2, 64, 64)])
+def test_512_sequences_mixed_lengths(hq, hkv, D, part):
+    """A serving-size batch: 512 sequences, lengths 0..600 (about a tenth empty), so every wave's
+    range crosses many sequences and the lookups walk the lengths 64 at a time; VALU (MHA) and
+    matrix-core (groups of 8 and 4) paths, balanced split and fixed partitions."""
+    _say(f"512 sequences Hq={hq} Hkv={hkv} D={D} part={part}")
+    rng = np.random.default_rng(512 + hq + D + part)
+    lens = rng.integers(0, 601, size=512)
+    lens[rng.random(512) < 0.1] = 0
+    cfg = _cfg(name="b512", num_seqs=512, num_heads=hq, num_kv_heads=hkv, head_dim=D, len_args=tuple(int(x) for x in lens),
+               q_dtype="bf16", cache_dtype="bf16", seed=14, partition_size=part)
+    _run_and_check(cfg, what=f"B=512 G={hq // hkv} part={part}")
+
+
 @pytest.mark.parametrize("hq,hkv", [(16, 4), (8, 8)])
 def test_balanced_split_reused_workspace_repeats_bitwise(hq, hkv):
     _say(f"balanced: reused workspace, repeat bitwise, Hq={hq} Hkv={hkv}")
