@@ -12,8 +12,10 @@ Timing: W untimed steps, then K timed steps between two device
 synchronisations; each step uses the next of R pool replicas (R * pool bytes
 well above the 256 MB Infinity Cache), so the KV bytes come from HBM.  Kernels
 are launched from Python on torch's current stream (--graphs replays captured
-HIP graphs of the same launches instead).  HIP events on the launch stream
-bracket every decode call for the roofline line.
+HIP graphs of the same launches instead).  One pair of HIP events on the launch
+stream brackets the K timed steps: the GPU time of one call for the roofline
+line (the default step is one pa_decode_append call).  A separate, shorter pass
+with events around every call gives the spread of one call's duration.
 
 Prints one JSON line.
 """
@@ -103,8 +105,17 @@ def measured_traffic(workload):
     return int(fields["traffic_bytes_per_call"]) if h.hexdigest() == fields["kernel_sources_sha256"] else None
 
 
+def append_bytes(w):
+    """Bytes the append of a step moves: the new K/V rows read (query dtype) and written into the
+    cache (plus one scale per token and pool for FP8)."""
+    cfg = w.cfg
+    eb = 1 if cfg.cache_dtype == "fp8_e4m3" else 2
+    rows = cfg.num_seqs * cfg.num_kv_heads * cfg.head_dim
+    return 2 * rows * 2 + 2 * rows * eb + (2 * 4 * cfg.num_seqs if eb == 1 else 0)
+
+
 def time_workload(name, steps, warmup, replicas, sample=None, partition_size=None, use_graphs=False, window=0,
-                  q_len=1, shared_prefix=False):
+                  q_len=1, shared_prefix=False, fused=False):
     import torch
     import paged_kv_cache_187_amd as pa
     import synth
@@ -139,11 +150,18 @@ def time_workload(name, steps, warmup, replicas, sample=None, partition_size=Non
         ws = pa.alloc_workspace(w.query, cfg.num_kv_heads, w.max_context_len, part)
     out = torch.empty_like(query)
 
+    assert not (fused and (q_len > 1 or shared_prefix or window > 0)), "the fused step is the plain decode"
+
     def append(r):
-        pa.pa_append_kv(w.key_new, w.value_new, kcs[r], vcs[r], w.slot_mapping, kss[r], vss[r])
+        if not fused:   # the fused step appends inside the decode call
+            pa.pa_append_kv(w.key_new, w.value_new, kcs[r], vcs[r], w.slot_mapping, kss[r], vss[r])
 
     def decode(r):
-        if q_len > 1:
+        if fused:
+            pa.pa_decode_append(out, w.query, w.key_new, w.value_new, kcs[r], vcs[r], w.block_tables,
+                                w.context_lens, cfg.scale, max_len, partition_size=part, k_scale=kss[r],
+                                v_scale=vss[r], workspace=ws)
+        elif q_len > 1:
             pa.pa_decode_multi(out, query, kcs[r], vcs[r], w.block_tables, w.context_lens, cfg.scale, max_len,
                                partition_size=part, k_scale=kss[r], v_scale=vss[r], workspace=ws)
         elif shared_prefix:
@@ -180,31 +198,52 @@ def time_workload(name, steps, warmup, replicas, sample=None, partition_size=Non
         run_append, run_decode = append, decode
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    # Timed region: `steps` whole steps with one event pair around all of them on the launch
+    # stream (events around every call put their own packets between the steps and slow each
+    # step by several microseconds).
+    region = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    region[0].record(stream)
     for i in range(steps):
         r = (warmup + i) % replicas
+        run_append(r)
+        run_decode(r)
+    region[1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    step_gpu_ms = region[0].elapsed_time(region[1]) / steps
+    # A separate pass with events around each decode call: the spread of one call's duration,
+    # and for a step of two calls the decode call alone.
+    n_ev = min(steps, 60)
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
+    for i in range(n_ev):
+        r = (warmup + steps + i) % replicas
         run_append(r)
         events[i][0].record(stream)
         run_decode(r)
         events[i][1].record(stream)
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
     dec_ms = sorted(e[0].elapsed_time(e[1]) for e in events)
     n = len(dec_ms)
     return {
         "w": w,
         "cpu_sample": host,
         "ms_per_step": (t1 - t0) * 1e3 / steps,
-        "decode_ms_mean": sum(dec_ms) / n,
+        "step_gpu_ms": step_gpu_ms,
+        # the fused step is one call: its duration is the region's; otherwise the per-call events'
+        "decode_ms_mean": step_gpu_ms if fused else sum(dec_ms) / n,
+        "decode_timing": ("events around the timed steps (the step is the call)" if fused
+                          else "events around each decode call (separate pass)"),
         "decode_ms_p10": dec_ms[n // 10],
         "decode_ms_p50": dec_ms[n // 2],
         "decode_ms_p90": dec_ms[min(n - 1, (9 * n) // 10)],
         "partition_size": pa.decode_partition_size(cfg.num_seqs, cfg.num_heads, cfg.num_kv_heads, cfg.head_dim,
                                                    max_len, part),
-        "bytes": algorithmic_bytes(w, window) + (q_len - 1) * cfg.num_seqs * cfg.num_heads * cfg.head_dim * 2,
+        "bytes": algorithmic_bytes(w, window) + (q_len - 1) * cfg.num_seqs * cfg.num_heads * cfg.head_dim * 2
+                 + (append_bytes(w) if fused else 0),
         "q_len": q_len,
+        "fused": fused,
     }
 
 
@@ -224,10 +263,13 @@ def read_ceiling(steps=50, warmup=5):
 
     stream: a plain streaming read of a 2 GiB buffer.  paged_gather: the llama7b decode's
     access pattern without the attention (every head's 256-byte rows of 16-token blocks of 32
-    KV heads, blocks in random order, 2048 waves, next block's loads in flight), 4400 blocks
-    (577 MB) per launch.  paged_gather_by_workload: the same probe in the geometry of the
-    gqa70b (8 KV heads, 256-byte rows) and fp8beams (8 KV heads, 128-byte rows of one-byte
-    codes) workloads, over as many block reads as the workload's K and V pools hold unique
+    KV heads, blocks in random order, next block's loads in flight) in the decode's order
+    (teams of one wave per KV head reading the same blocks; 1024 waves, the decode's count for
+    a 16-bit cache), 4400 blocks (577 MB) per launch; paged_gather_head_major: the same rows
+    with each wave reading one head of consecutive blocks (2048 waves).
+    paged_gather_by_workload: the team-order probe in the geometry of the gqa70b (8 KV heads,
+    256-byte rows, 1024 waves) and fp8beams (8 KV heads, 128-byte rows of one-byte codes, 2048
+    waves) workloads, over as many block reads as the workload's K and V pools hold unique
     blocks (the FP8 scales aside).  Each launch takes its blocks from one of three disjoint
     sets of a 2 GiB pool.  Probe kernels of libpaprobe.so
     (paged_kv_cache_187_amd/probe/pa_probe.hip), timed with HIP events.
@@ -239,12 +281,13 @@ def read_ceiling(steps=50, warmup=5):
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     lib.pa_probe_stream.argtypes = [vp, i64, vp, i32, vp]
     lib.pa_probe_gather.argtypes = [vp, vp, i32, i32, i32, i64, i32, vp, vp]
+    lib.pa_probe_gather_teams.argtypes = [vp, vp, i32, i32, i32, i64, i32, vp, vp]
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
     nbytes = 2 << 30
     buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
-    waves, blocks = 2048, 4096
-    sink = torch.empty(max(blocks * 256, waves * 64), dtype=torch.int32, device="cuda")
+    blocks = 4096
+    sink = torch.empty(max(blocks * 256, 2048 * 64), dtype=torch.int32, device="cuda")
     g = torch.Generator().manual_seed(7)
 
     def run(launch, n):
@@ -258,26 +301,29 @@ def read_ceiling(steps=50, warmup=5):
         torch.cuda.synchronize()
         return sorted(a.elapsed_time(b) for a, b in ev)[n // 2] * 1e-3
 
-    def gather(hkv, row, n_ids):
+    def gather(hkv, row, n_ids, waves, teams=True):
         blk = 16 * hkv * row
         num_blocks = nbytes // blk
-        assert 3 * n_ids <= num_blocks
+        assert 3 * n_ids <= num_blocks and waves * 64 <= sink.numel()
         perm = torch.randperm(num_blocks, generator=g)[:3 * n_ids].to(torch.int32).cuda()
         id_sets = [perm[i * n_ids:(i + 1) * n_ids].contiguous() for i in range(3)]
-        t = run(lambda i: lib.pa_probe_gather(buf.data_ptr(), id_sets[i % 3].data_ptr(), n_ids, hkv, row,
-                                              num_blocks, waves, sink.data_ptr(), sp), steps)
+        probe = lib.pa_probe_gather_teams if teams else lib.pa_probe_gather
+        t = run(lambda i: probe(buf.data_ptr(), id_sets[i % 3].data_ptr(), n_ids, hkv, row, num_blocks, waves,
+                                sink.data_ptr(), sp), steps)
         gathered = n_ids * blk
+        order = "teams of one wave per KV head on the same blocks" if teams else "one head per wave, head-major"
         return {"bytes": gathered, "GBs": round(gathered / t / 1e9, 1),
                 "frac_of_peak": round(gathered / t / 1e9 / HBM_PEAK_GBS, 4),
                 "pattern": f"{row}-byte head rows of random 16-token blocks, {hkv} KV heads, {n_ids} block reads, "
-                           f"{waves} waves"}
+                           f"{waves} waves, {order}"}
 
     t_stream = run(lambda i: lib.pa_probe_stream(buf.data_ptr(), nbytes, sink.data_ptr(), blocks, sp), steps)
     res = {"stream_read": {"bytes": nbytes, "GBs": round(nbytes / t_stream / 1e9, 1),
                            "frac_of_peak": round(nbytes / t_stream / 1e9 / HBM_PEAK_GBS, 4)},
-           "paged_gather": gather(32, 256, 4400),
-           "paged_gather_by_workload": {"gqa70b": gather(8, 256, 2 * unique_blocks("gqa70b")),
-                                        "fp8beams": gather(8, 128, 2 * unique_blocks("fp8beams"))}}
+           "paged_gather": gather(32, 256, 4400, 1024),
+           "paged_gather_head_major": gather(32, 256, 4400, 2048, teams=False),
+           "paged_gather_by_workload": {"gqa70b": gather(8, 256, 2 * unique_blocks("gqa70b"), 1024),
+                                        "fp8beams": gather(8, 128, 2 * unique_blocks("fp8beams"), 2048)}}
     del buf
     torch.cuda.empty_cache()
     return res
@@ -524,12 +570,16 @@ def summarize(name, r):
         "workload": name,
         "tokens_per_s": round(cfg.num_seqs * r.get("q_len", 1) / (r["ms_per_step"] * 1e-3), 1),
         "ms_per_step": round(r["ms_per_step"], 5),
+        "step_gpu_us": round(r["step_gpu_ms"] * 1e3, 2),
         "decode_us_mean": round(r["decode_ms_mean"] * 1e3, 2),
-        "decode_us_p10_p50_p90": [round(r[k] * 1e3, 2) for k in ("decode_ms_p10", "decode_ms_p50", "decode_ms_p90")],
+        "decode_timing": r["decode_timing"],
+        "decode_us_p10_p50_p90_per_call_events": [round(r[k] * 1e3, 2) for k in ("decode_ms_p10", "decode_ms_p50",
+                                                                                   "decode_ms_p90")],
         "algorithmic_bytes": r["bytes"],
         "effective_GBs": round(achieved, 1),
         "frac_of_peak": round(achieved / HBM_PEAK_GBS, 4),
         "partition_size": r["partition_size"],
+        "step": "pa_decode_append" if r.get("fused") else "pa_append_kv + decode call",
         **({"logical_bytes": logical_bytes(r["w"])} if cfg.beams > 1 else {}),
     }
 
@@ -570,6 +620,9 @@ def main():
                     help="sliding window (tokens) of the extra pa_decode_sliding line on the main workload; 0 = skip")
     ap.add_argument("--shared-prefix", action="store_true",
                     help="time the main workload (one with shared-prefix beams) through pa_decode_shared_prefix")
+    ap.add_argument("--unfused", action="store_true",
+                    help="time the step as pa_append_kv + pa_decode instead of pa_decode_append (one call); "
+                         "the default run also reports the unfused step of the main workload")
     ap.add_argument("--partition-size", type=int, default=None,
                     help="override the workload's partition length (tokens; 0 = library's choice)")
     args = ap.parse_args()
@@ -610,9 +663,10 @@ def main():
         return CPU_SAMPLE_HEADS.get(name, 0)
 
     cpu_samples = {}
+    fused = not (args.unfused or args.shared_prefix)
     main_r = time_workload(args.workload, args.steps, args.warmup, args.replicas, sample=sample_of(args.workload),
                            partition_size=args.partition_size, use_graphs=args.graphs,
-                           shared_prefix=args.shared_prefix)
+                           shared_prefix=args.shared_prefix, fused=fused)
     s = summarize(args.workload, main_r)
     cfg = main_r["w"].cfg
     if oracle_pool is not None:
@@ -620,7 +674,7 @@ def main():
     also = {}
     for name in [n for n in args.also.split(",") if n and n != args.workload]:
         r = time_workload(name, args.steps, args.warmup, args.replicas, sample=sample_of(name),
-                          partition_size=args.partition_size, use_graphs=args.graphs)
+                          partition_size=args.partition_size, use_graphs=args.graphs, fused=fused)
         if oracle_pool is not None:
             cpu_samples[name] = r["cpu_sample"]
         also[name] = summarize(name, r)
@@ -635,6 +689,12 @@ def main():
             del r
             torch.cuda.empty_cache()
 
+    if fused:
+        r = time_workload(args.workload, args.steps, args.warmup, args.replicas, partition_size=args.partition_size,
+                          use_graphs=args.graphs)
+        also[f"{args.workload}_unfused"] = summarize(args.workload, r)
+        del r
+        torch.cuda.empty_cache()
     if args.multi > 1:
         r = time_workload(args.workload, args.steps, args.warmup, args.replicas, partition_size=args.partition_size,
                           use_graphs=args.graphs, q_len=args.multi)
@@ -676,10 +736,14 @@ def main():
             "head_dim": cfg.head_dim, "block_size": 16, "kv_dtype": cfg.cache_dtype, "q_dtype": cfg.q_dtype,
             "accumulate": "f32", "partition_size": s["partition_size"], "pool_replicas": args.replicas,
             "hip_graphs": args.graphs,
+            "step": ("one pa_decode_append call (append fused into the decode)" if fused
+                     else "pa_append_kv + pa_decode" if not args.shared_prefix
+                     else "pa_append_kv + pa_decode_shared_prefix"),
             "tokens_in_cache": int(main_r["w"].lens_np.sum()),
         },
         "roofline": {
-            "kernel": "pa_decode (decode_kernel + decode_merge_kernel)",
+            "kernel": ("pa_decode_append (decode_kernel with the append fused in + decode_merge_kernel)" if fused
+                       else "pa_decode (decode_kernel + decode_merge_kernel)"),
             "bound": "hbm",
             "achieved": s["effective_GBs"],
             "peak": HBM_PEAK_GBS,
@@ -688,7 +752,8 @@ def main():
             "traffic": measured_traffic(args.workload + ("_shared_prefix" if args.shared_prefix else "")),
             "bytes_per_launch": s["algorithmic_bytes"],
             "launch_us_mean": s["decode_us_mean"],
-            "launch_us_p10_p50_p90": s["decode_us_p10_p50_p90"],
+            "launch_timing": s["decode_timing"],
+            "launch_us_p10_p50_p90_per_call_events": s["decode_us_p10_p50_p90_per_call_events"],
         },
         "also": also,
         # achievable read bandwidth on this machine (probe kernels), labelled apart from the decode

@@ -18,6 +18,8 @@
  *    pa_decode_sliding restricts it to a sliding window of recent tokens;
  *    pa_decode_multi takes several new tokens per sequence (causal).
  *
+ *  - pa_decode_append: both in one call (the append fused into the decode).
+ *
  *  - pa_copy_blocks: copy whole physical blocks, the copy-on-write step the
  *    block manager takes before a sequence writes into a block that other
  *    sequences share ("大模型推理引擎优化：…", §4.2; "LLM推理引擎深度实战：…", §2.2).
@@ -242,6 +244,41 @@ pa_status pa_decode(void *out, const void *query,
                     int32_t q_dtype, int32_t cache_dtype,
                     void *workspace, size_t workspace_bytes,
                     void *stream);
+
+/*
+ * pa_decode_append - one whole decode step in one call: the slot-mapped append of each
+ * sequence's new token ("大模型推理引擎优化：KV Cache 与连续批处理", §2.1-§2.2: each step adds
+ * the new token's K/V to the cache the step attends over), then pa_decode over the cache
+ * that now holds it.
+ *
+ * Sequence b with L = context_lens[b] (clamped as for pa_decode) > 0 has its new token at
+ * position L - 1: row (L - 1) % 16 of physical block block_tables[b, (L - 1) / 16].
+ * key_new / value_new: [num_seqs, num_kv_heads, head_dim] in q_dtype.  For a 16-bit cache
+ * (cache_dtype == q_dtype) the rows are copied bit for bit; for an FP8 cache they are
+ * quantised exactly as pa_append_kv quantises them (per-token scale amax / 448 over all
+ * num_kv_heads * head_dim values, written to k_scale / v_scale).  Afterwards the caches (and
+ * scales) are bit for bit what pa_append_kv with slot_mapping[b] = block * 16 + offset of
+ * that position (negative for L == 0) leaves, and `out` is bit for bit what pa_decode then
+ * returns.  Sequences with L == 0 append nothing; a table entry outside [0, num_blocks) is
+ * not written.  The kernels take the new token's K/V from key_new / value_new, not from its
+ * slot, so the slot's old contents never reach `out`; the block holding a new token must not
+ * be read by another sequence in the same call (a block is private before anyone writes into
+ * it: copy-on-write, pa_copy_blocks).  Every other argument, the workspace
+ * (pa_decode_workspace_bytes), determinism and errors are those of pa_decode; key_new and
+ * value_new must be 16-byte aligned (PA_ERR_ALIGN) and non-null (PA_ERR_NULL).
+ */
+pa_status pa_decode_append(void *out, const void *query,
+                           const void *key_new, const void *value_new,
+                           void *key_cache, void *value_cache,
+                           float *k_scale, float *v_scale,
+                           const int32_t *block_tables, const int32_t *context_lens,
+                           int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int64_t num_blocks,
+                           int32_t max_blocks_per_seq, int32_t max_context_len,
+                           float scale, int32_t partition_size,
+                           int32_t q_dtype, int32_t cache_dtype,
+                           void *workspace, size_t workspace_bytes,
+                           void *stream);
 
 /*
  * pa_decode_noalloc - pa_decode for callers that cannot allocate device memory (code

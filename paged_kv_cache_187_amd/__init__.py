@@ -18,6 +18,7 @@ from .binding import (  # noqa: F401
     pa_append_kv,
     pa_copy_blocks,
     pa_decode,
+    pa_decode_append,
     pa_decode_multi,
     pa_decode_noalloc,
     pa_decode_shared_prefix,

@@ -55,6 +55,8 @@ def load_library(path=LIB_PATH):
     lib.pa_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i64, i32, i32,
                               ctypes.c_float, i32, i32, i32, vp, sz, vp]
     lib.pa_decode.restype = i32
+    lib.pa_decode_append.argtypes = [vp, vp, vp, vp] + lib.pa_decode.argtypes[2:]
+    lib.pa_decode_append.restype = i32
     lib.pa_decode_noalloc.argtypes = lib.pa_decode.argtypes[:19] + [vp]
     lib.pa_decode_noalloc.restype = i32
     lib.pa_decode_sliding.argtypes = lib.pa_decode.argtypes + [i32]
@@ -199,6 +201,32 @@ def pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, sc
     """
     return _decode(None, out, query, key_cache, value_cache, block_tables, context_lens, scale, max_context_len,
                    partition_size, k_scale, v_scale, workspace, stream)
+
+
+def pa_decode_append(out, query, key_new, value_new, key_cache, value_cache, block_tables, context_lens, scale,
+                     max_context_len, partition_size=0, k_scale=None, v_scale=None, workspace=None, stream=None):
+    """One decode step in one call: writes key_new/value_new [B, Hkv, D] (query dtype) as each
+    sequence's token at position context_lens[b] - 1 (quantised for an FP8 cache), then decodes."""
+    _on_gpu(out, query, key_new, value_new, key_cache, value_cache, block_tables, context_lens, k_scale, v_scale,
+            workspace)
+    B, hq, d = query.shape
+    nb, bs, hkv, dk = key_cache.shape
+    if out.shape != query.shape or out.dtype != query.dtype or bs != BLOCK_SIZE or dk != d or \
+            value_cache.shape != key_cache.shape or block_tables.dim() != 2 or \
+            block_tables.shape[0] != B or context_lens.shape != (B,) or \
+            block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32 or \
+            key_new.shape != (B, hkv, d) or value_new.shape != key_new.shape or \
+            key_new.dtype != query.dtype or value_new.dtype != query.dtype:
+        raise ValueError("inconsistent shapes for pa_decode_append")
+    if workspace is None:
+        workspace = alloc_workspace(query, hkv, max_context_len, partition_size)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().pa_decode_append(
+        _ptr(out), _ptr(query), _ptr(key_new), _ptr(value_new), _ptr(key_cache), _ptr(value_cache), _ptr(k_scale),
+        _ptr(v_scale), _ptr(block_tables), _ptr(context_lens), B, hq, hkv, d, nb, block_tables.shape[1],
+        int(max_context_len), float(scale), int(partition_size), _DTYPE[query.dtype], _DTYPE[key_cache.dtype],
+        _ptr(workspace), ws_bytes, _stream(stream)))
+    return out
 
 
 def pa_decode_noalloc(out, query, key_cache, value_cache, block_tables, context_lens, scale, max_context_len,

@@ -15,7 +15,12 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 # Read-bandwidth probes (bench.py's ceiling line only; not part of the C ABI above).
 PROBE_SRC = os.path.join(PKG, "probe", "pa_probe.hip")
 PROBE_PATH = os.path.join(PKG, "libpaprobe.so")
-SOURCES = ["pa_append.hip", "pa_copy.hip", "pa_decode.hip", "pa_scratch.hip", "pa_api.cpp"]
+# (source, object, extra flags): the decode source is built twice, the second time for the
+# kernels of the fused append + decode.
+SOURCES = [("pa_append.hip", "pa_append.o", []), ("pa_copy.hip", "pa_copy.o", []),
+           ("pa_decode.hip", "pa_decode.o", []),
+           ("pa_decode.hip", "pa_decode_append.o", ["-DPA_DECODE_APPEND=1"]),
+           ("pa_scratch.hip", "pa_scratch.o", []), ("pa_api.cpp", "pa_api.o", [])]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 COMMON = [
@@ -47,11 +52,11 @@ def build(verbose=False, extra_flags=()):
     os.makedirs(BUILD, exist_ok=True)
     objs = []
     cmds = []
-    for src in SOURCES:
-        obj = os.path.join(BUILD, src.rsplit(".", 1)[0] + ".o")
+    for src, obj_name, flags in SOURCES:
+        obj = os.path.join(BUILD, obj_name)
         objs.append(obj)
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmds.append([HIPCC, *COMMON, *extra_flags, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([HIPCC, *COMMON, *extra_flags, *flags, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     tmp = LIB_PATH + ".tmp"

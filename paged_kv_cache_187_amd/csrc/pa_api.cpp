@@ -146,7 +146,8 @@ pa_status decode_impl(void* out, const void* query, const void* key_cache, const
                     int32_t head_dim, int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
                     float scale, int32_t partition_size, int32_t q_dtype, int32_t cache_dtype, void* workspace,
                     size_t workspace_bytes, void* stream, int32_t window, int32_t q_len,
-                    int32_t seq_group = 0, const int32_t* prefix_blocks = nullptr, bool use_scratch = false) {
+                    int32_t seq_group = 0, const int32_t* prefix_blocks = nullptr, bool use_scratch = false,
+                    const void* new_key = nullptr, const void* new_value = nullptr) {
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 ||
         num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || num_heads > 65536)
         return PA_ERR_SHAPE;
@@ -164,6 +165,9 @@ pa_status decode_impl(void* out, const void* query, const void* key_cache, const
     if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens) return PA_ERR_NULL;
     if (seq_group > 0 && !prefix_blocks) return PA_ERR_NULL;
     if (fp8 && (!k_scale || !v_scale)) return PA_ERR_NULL;
+    const bool fused = new_key != nullptr || new_value != nullptr;
+    if (fused && (!new_key || !new_value)) return PA_ERR_NULL;
+    if (fused && (!aligned(new_key, 16) || !aligned(new_value, 16))) return PA_ERR_ALIGN;
     if (use_scratch) {
         workspace = nullptr;
         workspace_bytes = 0;
@@ -216,6 +220,19 @@ pa_status decode_impl(void* out, const void* query, const void* key_cache, const
     p.scale_log2 = scale * 1.4426950408889634f;
     p.sgroup = seq_group;
     p.prefix_blocks = seq_group > 0 ? prefix_blocks : nullptr;
+    if (fused && fp8) {
+        // an FP8 cache's quantising append runs first, as its own kernel, at the slots the page
+        // tables give; then the plain decode
+        const hipError_t e = pa::launch_append_fp8_at_lengths(
+            new_key, new_value, (void*)key_cache, (void*)value_cache, (float*)k_scale, (float*)v_scale, block_tables,
+            context_lens, num_seqs, max_blocks_per_seq, p.ctx_limit, num_kv_heads * head_dim,
+            num_blocks * PA_BLOCK_SIZE, q_dtype, (hipStream_t)stream);
+        if (e != hipSuccess) return PA_ERR_HIP;
+        return from_hip(pa::launch_decode(p, head_dim, q_dtype, cache_dtype, (hipStream_t)stream));
+    }
+    p.new_key = new_key;
+    p.new_value = new_value;
+    if (fused) return from_hip(pa::launch_decode_append(p, head_dim, q_dtype, cache_dtype, (hipStream_t)stream));
     return from_hip(pa::launch_decode(p, head_dim, q_dtype, cache_dtype, (hipStream_t)stream));
 }
 
@@ -329,6 +346,20 @@ pa_status pa_decode(void* out, const void* query, const void* key_cache, const v
     return decode_impl(out, query, key_cache, value_cache, k_scale, v_scale, block_tables, context_lens, num_seqs,
                        num_heads, num_kv_heads, head_dim, num_blocks, max_blocks_per_seq, max_context_len, scale,
                        partition_size, q_dtype, cache_dtype, workspace, workspace_bytes, stream, 0, 1);
+}
+
+pa_status pa_decode_append(void* out, const void* query, const void* key_new, const void* value_new,
+                           void* key_cache, void* value_cache, float* k_scale, float* v_scale,
+                           const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                           int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                           int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                           int32_t partition_size, int32_t q_dtype, int32_t cache_dtype, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    if (!key_new || !value_new) return PA_ERR_NULL;
+    return decode_impl(out, query, key_cache, value_cache, k_scale, v_scale, block_tables, context_lens, num_seqs,
+                       num_heads, num_kv_heads, head_dim, num_blocks, max_blocks_per_seq, max_context_len, scale,
+                       partition_size, q_dtype, cache_dtype, workspace, workspace_bytes, stream, 0, 1, 0, nullptr,
+                       false, key_new, value_new);
 }
 
 pa_status pa_decode_noalloc(void* out, const void* query, const void* key_cache, const void* value_cache,

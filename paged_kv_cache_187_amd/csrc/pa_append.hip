@@ -32,6 +32,24 @@ __global__ __launch_bounds__(256) void append_copy_kernel(const uint4* __restric
     for (int i = threadIdx.x; i < row_vec; i += blockDim.x) dst[i] = src[i];
 }
 
+// Where token t goes: slots[t], or, without a slot list, the position L - 1 of sequence t
+// (L its length clamped to [0, ctx_limit]) through its page table; -1 for none.
+struct SlotSource {
+    const int64_t* slots;
+    const int32_t* tables;
+    const int32_t* lens;
+    int32_t max_blocks, ctx_limit;
+
+    __device__ int64_t slot(int64_t t) const {
+        if (slots) return slots[t];
+        int L = lens[t];
+        L = L < 0 ? 0 : (L > ctx_limit ? ctx_limit : L);
+        if (L == 0) return -1;
+        const int32_t phys = tables[t * max_blocks + (L - 1) / kBlockSize];
+        return phys < 0 ? -1 : (int64_t)phys * kBlockSize + (L - 1) % kBlockSize;
+    }
+};
+
 // Per-token E4M3 quantisation of one token's [Hkv, D] row.  Eight source
 // elements (16 bytes) per lane per step; codes are stored 8 bytes at a time.
 template <typename SRC>
@@ -41,11 +59,11 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(const uint4* __restrict
                                                          uint2* __restrict__ value_cache,
                                                          float* __restrict__ k_scale,
                                                          float* __restrict__ v_scale,
-                                                         const int64_t* __restrict__ slots,
+                                                         const SlotSource src_slots,
                                                          int32_t row_chunks, int64_t num_slots) {
     __shared__ float wave_max[256 / kWave];
     const int64_t t = blockIdx.x;
-    const int64_t slot = slots[t];
+    const int64_t slot = src_slots.slot(t);
     if (slot < 0 || slot >= num_slots) return;
     const bool is_v = blockIdx.y != 0;
     const uint4* src = (is_v ? value : key) + t * row_chunks;
@@ -106,20 +124,41 @@ hipError_t launch_append_copy(const void* key, const void* value, void* key_cach
     return hipGetLastError();
 }
 
-hipError_t launch_append_fp8(const void* key, const void* value, void* key_cache, void* value_cache,
-                             float* k_scale, float* v_scale, const int64_t* slots, int64_t num_tokens,
-                             int32_t row_elems, int64_t num_slots, int src_kind, hipStream_t stream) {
+namespace {
+
+hipError_t launch_fp8(const void* key, const void* value, void* key_cache, void* value_cache, float* k_scale,
+                      float* v_scale, const SlotSource& src, int64_t num_tokens, int32_t row_elems, int64_t num_slots,
+                      int src_kind, hipStream_t stream) {
     const int32_t chunks = row_elems / 8;
     const dim3 grid((uint32_t)num_tokens, 2);
     const dim3 block(threads_for(chunks));
     if (src_kind == kBF16) {
         hipLaunchKernelGGL(append_fp8_kernel<BF16>, grid, block, 0, stream, (const uint4*)key, (const uint4*)value,
-                           (uint2*)key_cache, (uint2*)value_cache, k_scale, v_scale, slots, chunks, num_slots);
+                           (uint2*)key_cache, (uint2*)value_cache, k_scale, v_scale, src, chunks, num_slots);
     } else {
         hipLaunchKernelGGL(append_fp8_kernel<F16>, grid, block, 0, stream, (const uint4*)key, (const uint4*)value,
-                           (uint2*)key_cache, (uint2*)value_cache, k_scale, v_scale, slots, chunks, num_slots);
+                           (uint2*)key_cache, (uint2*)value_cache, k_scale, v_scale, src, chunks, num_slots);
     }
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_append_fp8(const void* key, const void* value, void* key_cache, void* value_cache,
+                             float* k_scale, float* v_scale, const int64_t* slots, int64_t num_tokens,
+                             int32_t row_elems, int64_t num_slots, int src_kind, hipStream_t stream) {
+    return launch_fp8(key, value, key_cache, value_cache, k_scale, v_scale, SlotSource{slots, nullptr, nullptr, 0, 0},
+                      num_tokens, row_elems, num_slots, src_kind, stream);
+}
+
+hipError_t launch_append_fp8_at_lengths(const void* key, const void* value, void* key_cache, void* value_cache,
+                                        float* k_scale, float* v_scale, const int32_t* block_tables,
+                                        const int32_t* context_lens, int32_t num_seqs, int32_t max_blocks,
+                                        int32_t ctx_limit, int32_t row_elems, int64_t num_slots, int src_kind,
+                                        hipStream_t stream) {
+    return launch_fp8(key, value, key_cache, value_cache, k_scale, v_scale,
+                      SlotSource{nullptr, block_tables, context_lens, max_blocks, ctx_limit}, num_seqs, row_elems,
+                      num_slots, src_kind, stream);
 }
 
 }  // namespace pa

@@ -260,11 +260,63 @@ __device__ __forceinline__ int live_block(const DecodeParams& p, int tbl, int j,
     return (j < jend && phys >= 0 && phys < p.num_blocks) ? phys : -1;
 }
 
+template <int N> struct Bytes;
+template <> struct Bytes<4> { using T = uint32_t; };
+template <> struct Bytes<8> { using T = uint2; };
+template <> struct Bytes<16> { using T = uint4; };
+
+template <typename W>
+__device__ __forceinline__ void words_of(const W& w, uint32_t* out);
+template <>
+__device__ __forceinline__ void words_of<uint32_t>(const uint32_t& w, uint32_t* out) { out[0] = w; }
+template <>
+__device__ __forceinline__ void words_of<uint2>(const uint2& w, uint32_t* out) { out[0] = w.x; out[1] = w.y; }
+template <>
+__device__ __forceinline__ void words_of<uint4>(const uint4& w, uint32_t* out) {
+    out[0] = w.x; out[1] = w.y; out[2] = w.z; out[3] = w.w;
+}
+
+template <typename W>
+__device__ __forceinline__ W of_words(const uint32_t* w);
+template <>
+__device__ __forceinline__ uint32_t of_words<uint32_t>(const uint32_t* w) { return w[0]; }
+template <>
+__device__ __forceinline__ uint2 of_words<uint2>(const uint32_t* w) { return uint2{w[0], w[1]}; }
+template <>
+__device__ __forceinline__ uint4 of_words<uint4>(const uint32_t* w) { return uint4{w[0], w[1], w[2], w[3]}; }
+
+// Fused append (pa_decode_append, 16-bit caches).  The new token of sequence b sits at
+// position L - 1 of its last block; its K/V rows (new_key[b], new_value[b]: [Hkv, D], the
+// cache dtype) replace, in registers, what a wave loads from that slot, and the lanes that
+// hold those rows store them into the slot (one wave per (sequence, KV head)).  No wave reads
+// the slot's old contents or depends on when the store lands.  The pieces are loaded when
+// the segment starts and used only at its last block, so the loads wait for nothing.
+struct NewToken {
+    int o;      // offset of the token in its block
+    int jnew;   // logical block holding the token
+
+    static __device__ NewToken at(int L, int nblk) { return NewToken{(L - 1) % kBlockSize, nblk - 1}; }
+
+    // Address of byte `byte` of the new row of sequence b, KV head hk (K or V).
+    static __device__ const char* row(const void* base, const DecodeParams& p, int b, int hk, int D, int byte) {
+        return (const char*)base + (((int64_t)b * p.Hkv + hk) * D) * 2 + byte;
+    }
+
+    // Where a lane's piece of the new row goes in the cache (K or V pool), or null when the
+    // token's block is outside the pool.
+    static __device__ char* slot_row(void* pool, const DecodeParams& p, int b, int hk, int D, int jnew, int o,
+                                     int byte) {
+        const int phys = p.block_tables[(int64_t)b * p.max_blocks + jnew];
+        if (phys < 0 || phys >= p.num_blocks) return nullptr;
+        return (char*)pool + (((int64_t)phys * kBlockSize + o) * p.Hkv + hk) * D * 2 + byte;
+    }
+};
+
 // VALU path (head groups of 1, 2, 4 or 8 query heads).  One segment: blocks [jb, je) of
 // sequence b (nblk blocks, L tokens), head group hg.  Writes the output rows when the
 // segment is the whole sequence, else the partial for workspace slot `slot` (HPW
 // consecutive heads per slot).
-template <typename QT, typename CT, int D, int HPW, int NB>
+template <typename QT, typename CT, int D, int HPW, int NB, bool APPEND>
 struct ValuSegment {
 struct Buf {
     uint4 k[Layout<CT, D>::LPB], v[Layout<CT, D>::LPB];
@@ -291,6 +343,21 @@ static __device__ __forceinline__ void run(const DecodeParams& p, int lane, int 
     const int hk = h0 / (p.Hq / p.Hkv);
     const int row = lane / TPL;
     const int chunk = lane % TPL;
+
+    // Fused append: the segment that reads the sequence's last block loads this lane's 16 bytes
+    // of the new token's rows; at that block the lanes of the token's row take them, and in the
+    // first head group of each KV head also store them into the slot.
+    static_assert(!(APPEND && kFp8), "the fused append covers 16-bit caches");
+    NewToken nt{};
+    uint4 knew{}, vnew{};
+    const bool patch = APPEND && je == nblk && L > 0;
+    if constexpr (APPEND) {
+        if (patch) {
+            nt = NewToken::at(L, nblk);
+            knew = *(const uint4*)NewToken::row(p.new_key, p, b, hk, D, 16 * chunk);
+            vnew = *(const uint4*)NewToken::row(p.new_value, p, b, hk, D, 16 * chunk);
+        }
+    }
 
     // Query: this lane's EPL elements of each of the HPW heads.
     uint32_t qw[HPW][4];
@@ -365,10 +432,36 @@ static __device__ __forceinline__ void run(const DecodeParams& p, int lane, int 
 
     // Online-softmax update with the LPB tokens this row holds of block j.
     auto consume = [&](int j, const Buf& bf) {
-        const uint4(&kr)[LPB] = bf.k;
-        const uint4(&vr)[LPB] = bf.v;
-        const float(&ksc)[LPB] = bf.ks;
-        const float(&vsc)[LPB] = bf.vs;
+        uint4 kr[LPB], vr[LPB];
+        float ksc[LPB], vsc[LPB];
+#pragma unroll
+        for (int i = 0; i < LPB; ++i) {
+            kr[i] = bf.k[i];
+            vr[i] = bf.v[i];
+            ksc[i] = bf.ks[i];
+            vsc[i] = bf.vs[i];
+        }
+        if constexpr (APPEND) {
+            // the new token (row o of block jnew) comes from the inputs, not from its slot
+            if (patch && j == nt.jnew) {
+                const bool mine = row == nt.o % ROWS;
+#pragma unroll
+                for (int i = 0; i < LPB; ++i) {
+                    if (i == nt.o / ROWS && mine) {
+                        kr[i] = knew;
+                        vr[i] = vnew;
+                    }
+                }
+                if (mine && h0 % (p.Hq / p.Hkv) == 0) {
+                    char* kd = NewToken::slot_row((void*)p.key_cache, p, b, hk, D, nt.jnew, nt.o, 16 * chunk);
+                    char* vd = NewToken::slot_row((void*)p.value_cache, p, b, hk, D, nt.jnew, nt.o, 16 * chunk);
+                    if (kd) {
+                        *(uint4*)kd = knew;
+                        *(uint4*)vd = vnew;
+                    }
+                }
+            }
+        }
         bool valid[LPB];
 #pragma unroll
         for (int i = 0; i < LPB; ++i) {
@@ -524,21 +617,6 @@ static __device__ __forceinline__ void run(const DecodeParams& p, int lane, int 
 // FP8 caches are widened to the query's 16-bit type (exactly) before the products; the
 // per-token scales (four consecutive tokens per lane: one 16-byte load each for K and V)
 // multiply the scores and P.
-template <int N> struct Bytes;
-template <> struct Bytes<4> { using T = uint32_t; };
-template <> struct Bytes<8> { using T = uint2; };
-template <> struct Bytes<16> { using T = uint4; };
-
-template <typename W>
-__device__ __forceinline__ void words_of(const W& w, uint32_t* out);
-template <>
-__device__ __forceinline__ void words_of<uint32_t>(const uint32_t& w, uint32_t* out) { out[0] = w; }
-template <>
-__device__ __forceinline__ void words_of<uint2>(const uint2& w, uint32_t* out) { out[0] = w.x; out[1] = w.y; }
-template <>
-__device__ __forceinline__ void words_of<uint4>(const uint4& w, uint32_t* out) {
-    out[0] = w.x; out[1] = w.y; out[2] = w.z; out[3] = w.w;
-}
 
 // Max and sum over the four 16-lane groups (lanes c, c + 16, c + 32, c + 48), every
 // lane getting the result: gfx950's row and half-wave swaps, which stay in the VALU
@@ -563,7 +641,7 @@ constexpr float kSlack = 8.0f;
 
 // GROUPED: units of shared-prefix groups (rows = the group's sequences x heads); the
 // ungrouped instantiation carries none of that code.
-template <typename QT, typename CT, int D, int NB, bool GROUPED>
+template <typename QT, typename CT, int D, int NB, bool GROUPED, bool APPEND>
 struct MfmaSegment {
     using M = QT;
     static constexpr int EB = Storage<CT>::bytes;
@@ -735,6 +813,23 @@ struct MfmaSegment {
         char* kput = ktile + (lane / KLPR) * KRS + 16 * (lane % KLPR);
         const char* kget = ktile + c * KRS + 16 * g;
 
+        // Fused append (ungrouped units of one query, 16-bit cache): the segment that reads the
+        // sequence's last block loads this lane's pieces of the new token's rows (16 K bytes at the
+        // lane's K column, VBYTES V bytes at its V column); at that block the lanes of the token's
+        // row take them, and in the unit of the first heads of each KV head also store them.
+        static_assert(!(APPEND && (GROUPED || kFp8)), "the fused append covers ungrouped 16-bit units");
+        NewToken nt{};
+        uint4 knew{};
+        VT vnew{};
+        const bool patch = APPEND && je == nblk && L > 0;
+        if constexpr (APPEND) {
+            if (patch) {
+                nt = NewToken::at(L, nblk);
+                knew = *(const uint4*)NewToken::row(p.new_key, p, b, hk, D, 16 * (lane % KLPR));
+                vnew = *(const VT*)NewToken::row(p.new_value, p, b, hk, D, VBYTES * c);
+            }
+        }
+
         auto issue = [&](int j, int jend, int jbase, Buf& bf) {
             const int phys = live_block(p, tbl, j, jend, jbase);
             const bool ok = phys >= 0;
@@ -754,7 +849,32 @@ struct MfmaSegment {
             return ok;
         };
 
-        auto consume = [&](int j, const Buf& bf) {
+        auto consume = [&](int j, const Buf& bf0) {
+            Buf bf = bf0;
+            if constexpr (APPEND) {
+                // the new token (row o of block jnew) comes from the inputs, not from its slot
+                if (patch && j == nt.jnew) {
+                    const bool krow = lane / KLPR == nt.o % KTPL;
+                    const bool vrow = g == nt.o / 4;
+#pragma unroll
+                    for (int i = 0; i < KLOADS; ++i)
+                        if (i == nt.o / KTPL && krow) bf.k[i] = knew;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (i == nt.o % 4 && vrow) bf.v[i] = vnew;
+                    if (h0 % (p.Hq / p.Hkv) == 0) {
+                        if (krow) {
+                            char* kd = NewToken::slot_row((void*)p.key_cache, p, b, hk, D, nt.jnew, nt.o,
+                                                          16 * (lane % KLPR));
+                            if (kd) *(uint4*)kd = knew;
+                        }
+                        if (vrow) {
+                            char* vd = NewToken::slot_row((void*)p.value_cache, p, b, hk, D, nt.jnew, nt.o, VBYTES * c);
+                            if (vd) *(VT*)vd = vnew;
+                        }
+                    }
+                }
+            }
             // K rows -> LDS -> A operand (lane l: 16 bytes of token c at byte 64 i + 16 g, i.e.
             // 16-bit step s = i, or FP8 steps 2i and 2i + 1).  The tile belongs to this wave
             // alone; the fences keep the compiler from moving these accesses past each other.
@@ -1257,31 +1377,56 @@ hipError_t run(const DecodeParams& p, hipStream_t stream) {
 // Two blocks in flight per wave: deeper rings measured no faster.
 constexpr int kRing = 2;
 
-template <typename QT, typename CT, int D>
+// APPEND: kernels of the fused append + decode (one query per sequence, no shared-prefix groups).
+template <typename QT, typename CT, int D, bool APPEND>
 hipError_t run_path(const DecodeParams& p, hipStream_t s) {
-    if (p.mfma)
-        return p.sgroup > 0 ? run<QT, D, MfmaSegment<QT, CT, D, kRing, true>>(p, s)
-                            : run<QT, D, MfmaSegment<QT, CT, D, kRing, false>>(p, s);
+    if (p.mfma) {
+        if constexpr (!APPEND) {
+            if (p.sgroup > 0) return run<QT, D, MfmaSegment<QT, CT, D, kRing, true, false>>(p, s);
+        }
+        return run<QT, D, MfmaSegment<QT, CT, D, kRing, false, APPEND>>(p, s);
+    }
     switch (p.hpw) {
-        case 1: return run<QT, D, ValuSegment<QT, CT, D, 1, kRing>>(p, s);
-        case 2: return run<QT, D, ValuSegment<QT, CT, D, 2, kRing>>(p, s);
-        case 4: return run<QT, D, ValuSegment<QT, CT, D, 4, kRing>>(p, s);
-        case 8: return run<QT, D, ValuSegment<QT, CT, D, 8, kRing>>(p, s);
+        case 1: return run<QT, D, ValuSegment<QT, CT, D, 1, kRing, APPEND>>(p, s);
+        case 2: return run<QT, D, ValuSegment<QT, CT, D, 2, kRing, APPEND>>(p, s);
+        case 4: return run<QT, D, ValuSegment<QT, CT, D, 4, kRing, APPEND>>(p, s);
+        case 8: return run<QT, D, ValuSegment<QT, CT, D, 8, kRing, APPEND>>(p, s);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <typename QT, typename CT>
+template <typename QT, typename CT, bool APPEND>
 hipError_t run_d(const DecodeParams& p, int d, hipStream_t s) {
     switch (d) {
-        case 64: return run_path<QT, CT, 64>(p, s);
-        case 128: return run_path<QT, CT, 128>(p, s);
+        case 64: return run_path<QT, CT, 64, APPEND>(p, s);
+        case 128: return run_path<QT, CT, 128, APPEND>(p, s);
         default: return hipErrorInvalidValue;
     }
+}
+
+// The fused append covers 16-bit caches; an FP8 cache's append runs as its own kernel (the
+// per-token scale needs the whole token before any code is known).
+template <bool APPEND>
+hipError_t launch(const DecodeParams& p, int head_dim, int q_kind, int cache_kind, hipStream_t stream) {
+    if (q_kind == kF16 && cache_kind == kF16) return run_d<F16, F16, APPEND>(p, head_dim, stream);
+    if (q_kind == kBF16 && cache_kind == kBF16) return run_d<BF16, BF16, APPEND>(p, head_dim, stream);
+    if constexpr (!APPEND) {
+        if (q_kind == kF16 && cache_kind == kFP8) return run_d<F16, FP8, false>(p, head_dim, stream);
+        if (q_kind == kBF16 && cache_kind == kFP8) return run_d<BF16, FP8, false>(p, head_dim, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
 
+// This source is compiled twice: once for the plain decode kernels (PA_DECODE_APPEND unset)
+// and once for the fused append + decode kernels, so the two sets build in parallel.
+#if PA_DECODE_APPEND
+hipError_t launch_decode_append(const DecodeParams& p, int head_dim, int q_kind, int cache_kind,
+                                hipStream_t stream) {
+    return launch<true>(p, head_dim, q_kind, cache_kind, stream);
+}
+#else
 HeadGrouping head_grouping(int group) {
     // Groups of 3 to 16 heads (or multiples of 16) go to the matrix cores, padded to 16
     // rows; smaller groups stay on the VALU path.
@@ -1303,11 +1448,8 @@ HeadGrouping multi_query_grouping(int group) {
 }
 
 hipError_t launch_decode(const DecodeParams& p, int head_dim, int q_kind, int cache_kind, hipStream_t stream) {
-    if (q_kind == kF16 && cache_kind == kF16) return run_d<F16, F16>(p, head_dim, stream);
-    if (q_kind == kBF16 && cache_kind == kBF16) return run_d<BF16, BF16>(p, head_dim, stream);
-    if (q_kind == kF16 && cache_kind == kFP8) return run_d<F16, FP8>(p, head_dim, stream);
-    if (q_kind == kBF16 && cache_kind == kFP8) return run_d<BF16, FP8>(p, head_dim, stream);
-    return hipErrorInvalidValue;
+    return launch<false>(p, head_dim, q_kind, cache_kind, stream);
 }
+#endif
 
 }  // namespace pa

@@ -42,6 +42,11 @@ struct DecodeParams {
     // entries; a unit holds the group's sequences as tile rows.  sgroup == 0: no groups.
     int32_t sgroup;
     const int32_t* prefix_blocks;  // [B / sgroup]
+    // Fused append + decode (16-bit caches): the new token of sequence b (position L_b - 1) has
+    // K/V rows new_key[b], new_value[b] ([B, Hkv, D], the cache dtype), written into its slot by
+    // the decode kernel itself.  Null for the plain decode.
+    const void* new_key;
+    const void* new_value;
 };
 
 hipError_t launch_append_copy(const void* key, const void* value, void* key_cache, void* value_cache,
@@ -51,6 +56,14 @@ hipError_t launch_append_copy(const void* key, const void* value, void* key_cach
 hipError_t launch_append_fp8(const void* key, const void* value, void* key_cache, void* value_cache,
                              float* k_scale, float* v_scale, const int64_t* slots, int64_t num_tokens,
                              int32_t row_elems, int64_t num_slots, int src_kind, hipStream_t stream);
+
+// The quantising append of each sequence's new token at position L - 1 (L = context_lens[b]
+// clamped to [0, ctx_limit]; nothing for L == 0), the slot taken from the page table.
+hipError_t launch_append_fp8_at_lengths(const void* key, const void* value, void* key_cache, void* value_cache,
+                                        float* k_scale, float* v_scale, const int32_t* block_tables,
+                                        const int32_t* context_lens, int32_t num_seqs, int32_t max_blocks,
+                                        int32_t ctx_limit, int32_t row_elems, int64_t num_slots, int src_kind,
+                                        hipStream_t stream);
 
 // Whole-block copies from block src of the source pools to block dst of the destination
 // pools for (src, dst) pairs (FP8 scales too when the scale pointers are not null);
@@ -71,6 +84,9 @@ HeadGrouping head_grouping(int group);          // one query per sequence
 HeadGrouping multi_query_grouping(int group);  // several queries per sequence
 
 hipError_t launch_decode(const DecodeParams& p, int head_dim, int q_kind, int cache_kind, hipStream_t stream);
+// The same decode with the append of each sequence's new token fused in (new_key/new_value set).
+hipError_t launch_decode_append(const DecodeParams& p, int head_dim, int q_kind, int cache_kind,
+                                hipStream_t stream);
 
 // Device address of the fixed decode scratch on the current device (resolved once per
 // device); used only by pa_decode_noalloc.

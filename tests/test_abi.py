@@ -35,7 +35,7 @@ def lib():
 
 
 def test_header_declares_the_boundary():
-    assert _declared() == ["pa_append_kv", "pa_copy_blocks", "pa_decode", "pa_decode_multi",
+    assert _declared() == ["pa_append_kv", "pa_copy_blocks", "pa_decode", "pa_decode_append", "pa_decode_multi",
                            "pa_decode_multi_workspace_bytes", "pa_decode_noalloc", "pa_decode_partition_size",
                            "pa_decode_shared_prefix", "pa_decode_shared_prefix_workspace_bytes",
                            "pa_decode_sliding", "pa_decode_workspace_bytes", "pa_status_string", "pa_swap_blocks"]
@@ -163,6 +163,28 @@ def test_decode_host_checks(lib):
     assert _decode(lib, B=0) == OK                          # nothing to do, nothing launched
 
 
+def test_fused_append_decode_host_checks(lib):
+    def fa(**kw):
+        a = dict(out=FAKE, query=FAKE, kn=FAKE, vn=FAKE, key_cache=FAKE, value_cache=FAKE, k_scale=None,
+                 v_scale=None, block_tables=FAKE, context_lens=FAKE, B=2, Hq=8, Hkv=2, D=128, nb=10, mb=4, maxL=64,
+                 scale=0.1, part=0, qd=F16, cd=F16, ws=FAKE, wsb=1 << 30)
+        a.update(kw)
+        return lib.pa_decode_append(a["out"], a["query"], a["kn"], a["vn"], a["key_cache"], a["value_cache"],
+                                    a["k_scale"], a["v_scale"], a["block_tables"], a["context_lens"], a["B"],
+                                    a["Hq"], a["Hkv"], a["D"], a["nb"], a["mb"], a["maxL"], a["scale"], a["part"],
+                                    a["qd"], a["cd"], a["ws"], a["wsb"], None)
+    assert fa(kn=None) == NULL
+    assert fa(vn=None) == NULL
+    assert fa(kn=FAKE + 8) == ALIGN
+    assert fa(out=None) == NULL
+    assert fa(Hq=6, Hkv=4) == SHAPE
+    assert fa(D=96) == UNSUP
+    assert fa(qd=F16, cd=BF16) == DTYPE
+    assert fa(cd=FP8, qd=BF16) == NULL                      # FP8 cache without scales
+    assert fa(ws=None, wsb=0) == WS
+    assert fa(B=0) == OK                                    # nothing to do, nothing launched
+
+
 def test_noalloc_decode_host_checks(lib):
     """The no-allocation decode checks its arguments like pa_decode and rejects, before touching the
     device, any call whose workspace would not fit the fixed scratch (64 MiB)."""
@@ -262,14 +284,14 @@ def test_binding_rejects_host_tensors():
     assert ctypes.c_size_t(-1).value > 0
 
 
-def test_probe_library_exports_its_two_probes():
+def test_probe_library_exports_its_probes():
     # bench.py's read-bandwidth ceiling comes from a separate library, outside the C ABI.
     from paged_kv_cache_187_amd.build import PROBE_PATH
     if not os.path.exists(PROBE_PATH):
         pytest.fail("libpaprobe.so is not built (run __graft_entry__.build())")
     nm = subprocess.run(["nm", "-D", "--defined-only", PROBE_PATH], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in nm.splitlines() if line.strip()}
-    assert {"pa_probe_stream", "pa_probe_gather"} <= exported
+    assert {"pa_probe_stream", "pa_probe_gather", "pa_probe_gather_teams"} <= exported
     lib = ctypes.CDLL(PROBE_PATH)
     lib.pa_probe_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
     assert lib.pa_probe_stream(None, 16, None, 1, None) != 0      # rejected on the host, nothing launched
@@ -280,3 +302,6 @@ def test_probe_library_exports_its_two_probes():
         assert lib.pa_probe_gather(fake, fake, 16, 8, row, 64, 2048, fake, None) != 0
     assert lib.pa_probe_gather(fake, fake, 16, 1 << 20, 256, 64, 2048, fake, None) != 0   # block over 1 GiB
     assert lib.pa_probe_gather(None, fake, 16, 8, 128, 64, 2048, fake, None) != 0
+    lib.pa_probe_gather_teams.argtypes = [vp, vp, i32, i32, i32, i64, i32, vp, vp]
+    assert lib.pa_probe_gather_teams(fake, fake, 16, 8, 128, 64, 2044, fake, None) != 0   # waves % heads
+    assert lib.pa_probe_gather_teams(fake, fake, 16, 8, 64, 64, 2048, fake, None) != 0

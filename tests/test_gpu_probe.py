@@ -23,6 +23,7 @@ def _lib():
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     lib.pa_probe_stream.argtypes = [vp, i64, vp, i32, vp]
     lib.pa_probe_gather.argtypes = [vp, vp, i32, i32, i32, i64, i32, vp, vp]
+    lib.pa_probe_gather_teams.argtypes = [vp, vp, i32, i32, i32, i64, i32, vp, vp]
     return lib
 
 
@@ -57,6 +58,58 @@ def _gather_expected(words, ids, hkv, row, num_blocks, waves):
                     acc ^= words[off + k]
         out[w] = acc
     return out
+
+
+def _gather_teams_expected(words, ids, hkv, row, num_blocks, waves):
+    """The same XOR for the team order: wave w reads head w % hkv of id range w / hkv, the
+    ranges [r n / teams, (r + 1) n / teams) of the n ids."""
+    tok = hkv * row // 4
+    blk = 16 * tok
+    lpr = row // 16
+    rpl = 64 // lpr
+    n_ids = len(ids)
+    teams = waves // hkv
+    lane = np.arange(64)
+    base = (lane // lpr) * tok + (lane % lpr) * 4
+    out = np.zeros((waves, 64), dtype=np.uint32)
+    for w in range(waves):
+        head, r = w % hkv, w // hkv
+        acc = np.zeros(64, dtype=np.uint32)
+        for i in range(r * n_ids // teams, (r + 1) * n_ids // teams):
+            bid = int(ids[i])
+            if bid < 0 or bid >= num_blocks:
+                bid = 0
+            for ld in range(16 // rpl):
+                off = bid * blk + ld * rpl * tok + head * row // 4 + base
+                for k in range(4):
+                    acc ^= words[off + k]
+        out[w] = acc
+    return out
+
+
+@pytest.mark.parametrize("row,hkv,n_ids,waves", [
+    (128, 3, 37, 9),        # waves not a multiple of the 4 per workgroup
+    (256, 2, 29, 200),      # more teams than blocks: empty ranges
+    (128, 8, 64, 16),
+    (256, 8, 23, 64),
+])
+def test_gather_teams_probe_reads_every_row_it_claims(row, hkv, n_ids, waves):
+    _say(f"gather probe (teams) row={row} hkv={hkv} ids={n_ids} waves={waves}")
+    lib = _lib()
+    num_blocks = 50
+    rng = np.random.default_rng(row + hkv + n_ids + 1)
+    words = rng.integers(0, 1 << 32, size=num_blocks * 16 * hkv * row // 4, dtype=np.uint64).astype(np.uint32)
+    ids = rng.integers(0, num_blocks, size=n_ids).astype(np.int32)
+    ids[3] = -1                                # outside the pool: the probe reads block 0
+    ids[5] = num_blocks + 4
+    pool = torch.from_numpy(words.view(np.int32).copy()).cuda()
+    dids = torch.from_numpy(ids).cuda()
+    sink = torch.zeros(waves * 64, dtype=torch.int32, device="cuda")
+    assert lib.pa_probe_gather_teams(pool.data_ptr(), dids.data_ptr(), n_ids, hkv, row, num_blocks, waves,
+                                     sink.data_ptr(), None) == 0
+    torch.cuda.synchronize()
+    got = sink.cpu().numpy().view(np.uint32).reshape(waves, 64)
+    np.testing.assert_array_equal(got, _gather_teams_expected(words, ids, hkv, row, num_blocks, waves))
 
 
 @pytest.mark.parametrize("row,hkv,n_ids,waves", [
