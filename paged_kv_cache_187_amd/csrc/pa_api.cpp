@@ -16,12 +16,12 @@ namespace {
 
 constexpr int32_t kMaxPartition = 1 << 20;
 constexpr int64_t kMaxWork = ((int64_t)1 << 30);  // waves, or (head group, block) pairs, per launch
-// Waves of the balanced split.  A 16-bit cache block gives a wave twice the bytes per
-// instruction of an FP8 block: one wave per SIMD keeps the memory system saturated and
-// halves the split units; FP8 blocks need two waves per SIMD to overlap their conversions
-// with the loads.  Workspace queries size for the larger count (an upper bound).
-constexpr int64_t kBalancedWaves16 = 1024;          // 4 per CU
-constexpr int64_t kBalancedWavesFp8 = 2048;         // 8 per CU
+// Waves of the balanced split.  One wave per SIMD keeps the memory system saturated (the
+// matrix-core path streams two blocks per ring entry); on the VALU path an FP8 block
+// needs two waves per SIMD to overlap its conversions with the loads.  Workspace queries
+// size for the larger count (an upper bound).
+constexpr int64_t kBalancedWaves = 1024;            // 4 per CU
+constexpr int64_t kBalancedWavesValuFp8 = 2048;     // 8 per CU
 constexpr int32_t kMaxQueries = 4096;               // new tokens per sequence in one multi-query call
 
 // Launch shape shared by pa_decode and pa_decode_workspace_bytes.
@@ -44,7 +44,7 @@ struct Plan {
 // the group's sequences times the query heads of one KV head as rows of a 16-row tile.
 Plan make_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                int32_t max_context_len, int32_t partition_size, int32_t q_len = 1, int32_t seq_group = 0,
-               int64_t balanced_waves = kBalancedWavesFp8) {
+               bool fp8 = true) {
     Plan pl{};
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 || head_dim <= 0 ||
         max_context_len < 0 || partition_size < 0 || partition_size % PA_BLOCK_SIZE != 0 ||
@@ -72,6 +72,7 @@ Plan make_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_
         // Teams of one wave per head group share a range of (sequence, block) positions:
         // about balanced_waves waves, at most one team per block and at least one team.
         const int64_t blocks = entries * max_blocks;   // upper bound of (entry, block) positions
+        const int64_t balanced_waves = fp8 && !pl.mfma ? kBalancedWavesValuFp8 : kBalancedWaves;
         int64_t teams = balanced_waves / pl.groups;
         if (teams > blocks) teams = blocks;
         if (teams < 1) teams = 1;
@@ -157,7 +158,7 @@ pa_status decode_impl(void* out, const void* query, const void* key_cache, const
     if (!fp8 && cache_dtype != q_dtype) return PA_ERR_DTYPE;
     if (!std::isfinite(scale) || window < 0) return PA_ERR_SHAPE;
     const Plan pl = make_plan(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, partition_size, q_len,
-                              seq_group, fp8 ? kBalancedWavesFp8 : kBalancedWaves16);
+                              seq_group, fp8);
     if (!pl.ok) return PA_ERR_SHAPE;
     const size_t need = workspace_size(pl, head_dim);
     if (use_scratch && need > PA_NOALLOC_SCRATCH_BYTES) return PA_ERR_SCRATCH;

@@ -179,6 +179,42 @@ __device__ SeqPos locate(const DecodeParams& p, const SeqTable& st, int lane, in
     return {0, 0, 0};
 }
 
+// A wave's walk through the balanced order.  The lanes hold 64 consecutive entries
+// c .. c + 63: entry c + lane's clamped length (sequences; 0 for groups, whose segments
+// read their own lengths), block count and first position.  Positions only grow along a
+// wave's range, so the walk loads each chunk once and a new segment's entry is a ballot
+// over registers, with no memory access.
+struct Cursor {
+    int c, len, nb, start, end;   // end: the position after the chunk's last entry
+};
+
+__device__ Cursor cursor_chunk(const DecodeParams& p, int lane, int c, int carry) {
+    Cursor k;
+    const int n = num_entries(p);
+    const int b = c + lane;
+    k.c = c;
+    if (p.sgroup > 0) {
+        k.len = 0;
+        k.nb = b < n ? group_blocks(p, b) : 0;
+    } else {
+        k.len = b < n ? seq_len(p, b) : 0;
+        k.nb = k.len > 0 ? (k.len + kBlockSize - 1) / kBlockSize - first_token(p, k.len) / kBlockSize : 0;
+    }
+    const int incl = wave_incl_scan(k.nb, lane);
+    k.start = carry + incl - k.nb;
+    k.end = carry + __builtin_amdgcn_readlane(incl, kWave - 1);
+    return k;
+}
+
+// The non-empty entry holding position pos (0 <= pos < total blocks), moving the cursor on.
+__device__ SeqPos cursor_find(const DecodeParams& p, int lane, Cursor& k, int pos, int& len) {
+    while (pos >= k.end) k = cursor_chunk(p, lane, k.c + kWave, k.end);
+    const uint64_t mask = __ballot(k.nb > 0 && k.start <= pos);
+    const int lb = 63 - __builtin_clzll(mask);
+    len = __builtin_amdgcn_readlane(k.len, lb);
+    return {k.c + lb, __builtin_amdgcn_readlane(k.start, lb), __builtin_amdgcn_readlane(k.nb, lb)};
+}
+
 // Block count and exclusive block prefix of entry b (b wave-uniform).
 __device__ SeqPos seq_entry(const DecodeParams& p, const SeqTable& st, int lane, int b) {
     if (st.single) return {b, __builtin_amdgcn_readlane(st.start, b), __builtin_amdgcn_readlane(st.nb, b)};
@@ -224,30 +260,31 @@ __device__ Ranges make_ranges(const DecodeParams& p, int T) {
     return r;
 }
 
-// Streams logical blocks [jb, je) of one sequence through NB register buffers:
-// consume(j, buf) runs for every block in order while the loads of the next NB-1
-// blocks are in flight.  Every issue is unconditional (the compiler can then count
+// Streams logical blocks [jb, je) of one sequence through NB register buffers of STEP
+// blocks each: consume(j, buf) runs for blocks j .. j + STEP - 1 in order while the loads
+// of the next NB-1 buffers are in flight.  Every issue is unconditional (the compiler can then count
 // the loads and wait exactly for the oldest buffer): an issue for a block past the end
 // of the current 64-block chunk loads through an empty buffer descriptor, which
 // returns zeros without touching memory, and is never consumed.  The page table is
 // read 64 ids at a time, one per lane (`tbl`, refreshed by table_chunk);
 // issue(j, jend, jbase, buf) gets the chunk's end so it can tell live blocks apart.
-template <int NB, typename Buf, typename TableFn, typename IssueFn, typename ConsumeFn>
+template <int NB, int STEP, typename Buf, typename TableFn, typename IssueFn, typename ConsumeFn>
 __device__ __forceinline__ void stream_blocks(int jb, int je, int& tbl, TableFn table_chunk, IssueFn issue,
                                               ConsumeFn consume) {
+    static_assert(kWave % STEP == 0, "a buffer's blocks come from one table chunk");
     Buf buf[NB];
     bool ok[NB];
     for (int jc = jb; jc < je; jc += kWave) {
         if (jc != jb) tbl = table_chunk(jc);
         const int jend = min(je, jc + kWave);
 #pragma unroll
-        for (int k = 0; k < NB - 1; ++k) ok[k] = issue(jc + k, jend, jc, buf[k]);
-        for (int j = jc; j < jend; j += NB) {
+        for (int k = 0; k < NB - 1; ++k) ok[k] = issue(jc + STEP * k, jend, jc, buf[k]);
+        for (int j = jc; j < jend; j += NB * STEP) {
 #pragma unroll
             for (int k = 0; k < NB; ++k) {
                 const int nk = (k + NB - 1) % NB;
-                ok[nk] = issue(j + k + NB - 1, jend, jc, buf[nk]);
-                if (j + k < jend && ok[k]) consume(j + k, buf[k]);
+                ok[nk] = issue(j + STEP * (k + NB - 1), jend, jc, buf[nk]);
+                if (j + STEP * k < jend && ok[k]) consume(j + STEP * k, buf[k]);
             }
         }
     }
@@ -284,6 +321,16 @@ template <>
 __device__ __forceinline__ uint2 of_words<uint2>(const uint32_t* w) { return uint2{w[0], w[1]}; }
 template <>
 __device__ __forceinline__ uint4 of_words<uint4>(const uint32_t* w) { return uint4{w[0], w[1], w[2], w[3]}; }
+
+// One segment of a wave's range in the balanced split: blocks [jb, je) of sequence (or
+// group) b, jfirst .. nblk - 1 the blocks in play, lo the first token read, L the length
+// (0 for groups), the workspace slot of its partial and whether that partial waits in the
+// stash.
+struct SegInfo {
+    int b, jb, je, jfirst, nblk, lo, L;
+    int64_t slot;
+    bool defer;
+};
 
 // Fused append (pa_decode_append, 16-bit caches).  The new token of sequence b sits at
 // position L - 1 of its last block; its K/V rows (new_key[b], new_value[b]: [Hkv, D], the
@@ -325,8 +372,20 @@ struct Buf {
 // Partials are stored where they are produced (defer is ignored; nothing to flush).
 static __device__ __forceinline__ void flush(const DecodeParams&, int, int64_t) {}
 
+// What a segment needs before it can issue its first block: the page-table chunk of block
+// jb (lane i: the physical id of block jb + i).  Loaded one segment ahead, so a new segment
+// starts its loads without waiting on memory (its queries load alongside its first block).
+struct Pre {
+    int tbl;
+};
+static __device__ __forceinline__ Pre prefetch(const DecodeParams& p, int lane, int b, int /*hg*/, int jb) {
+    const int j = jb + lane;
+    return Pre{j < p.max_blocks ? p.block_tables[(int64_t)b * p.max_blocks + j] : -1};
+}
+
 static __device__ __forceinline__ void run(const DecodeParams& p, int lane, int b, int hg, int jb, int je,
-                                           int jfirst, int nblk, int lo, int L, int64_t slot, bool /*defer*/) {
+                                           int jfirst, int nblk, int lo, int L, int64_t slot, bool /*defer*/,
+                                           const Pre& pre) {
     using Ly = Layout<CT, D>;
     constexpr int EB = Ly::EB, EPL = Ly::EPL, TPL = Ly::TPL, ROWS = Ly::ROWS, LPB = Ly::LPB;
     constexpr bool kFp8 = EB == 1;
@@ -337,7 +396,7 @@ static __device__ __forceinline__ void run(const DecodeParams& p, int lane, int 
         const int j = jbase + lane;
         return j < p.max_blocks ? table[j] : -1;
     };
-    int tbl = table_chunk(jb);
+    int tbl = pre.tbl;
 
     const int h0 = hg * HPW;
     const int hk = h0 / (p.Hq / p.Hkv);
@@ -548,7 +607,7 @@ static __device__ __forceinline__ void run(const DecodeParams& p, int lane, int 
         }
     };
 
-    stream_blocks<NB, Buf>(jb, je, tbl, table_chunk, issue, consume);
+    stream_blocks<NB, 1, Buf>(jb, je, tbl, table_chunk, issue, consume);
 
     // Merge the ROWS row states (lanes with equal `chunk`); afterwards every row holds the
     // segment's result and the TPL lanes of row 0 write it.
@@ -661,6 +720,39 @@ struct MfmaSegment {
         VT v[4];
         float4 ks, vs;
     };
+    // The ring holds blocks in pairs: the P V product runs on 16x16x32 tiles, whose 32-deep
+    // contraction covers two blocks (k = 8 g + i is token 4 g + i % 4 of block i / 4; the
+    // score tiles put exactly those tokens in lane group g).  ok[q]: block q is in the pool
+    // and in the run (otherwise its loads returned zeros and its tokens are masked).
+    struct Pair {
+        Buf b[2];
+        bool ok[2];
+    };
+
+    // B operand of tile t for one block: V rows 4g .. 4g + 3, element t of the lane's E,
+    // as two words of operand-type pairs (rows 4g, 4g + 1 and rows 4g + 2, 4g + 3).
+    // 16-bit: w[i][k] holds elements 2k, 2k + 1 of row i; one byte permute per word.
+    static __device__ __forceinline__ uint2 v_tile16(const uint32_t (&w)[4][E / 2], int t) {
+        const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;   // high or low halves of both
+        const int k = t >> 1;
+        return uint2{__builtin_amdgcn_perm(w[1][k], w[0][k], sel), __builtin_amdgcn_perm(w[3][k], w[2][k], sel)};
+    }
+    // FP8: x01[u][h] holds codes (row 0, row 1) of elements 4u + 2h and 4u + 2h + 1, byte
+    // order r0, r1, r0, r1 (x23 the same for rows 2, 3), so one widening per word gives a pair.
+    static __device__ __forceinline__ void v_codes(const uint32_t (&w)[4][(VBYTES + 3) / 4],
+                                                   uint32_t (&x01)[(VBYTES + 3) / 4][2],
+                                                   uint32_t (&x23)[(VBYTES + 3) / 4][2]) {
+#pragma unroll
+        for (int u = 0; u < (VBYTES + 3) / 4; ++u) {
+            x01[u][0] = __builtin_amdgcn_perm(w[1][u], w[0][u], 0x05010400u);
+            x01[u][1] = __builtin_amdgcn_perm(w[1][u], w[0][u], 0x07030602u);
+            x23[u][0] = __builtin_amdgcn_perm(w[3][u], w[2][u], 0x05010400u);
+            x23[u][1] = __builtin_amdgcn_perm(w[3][u], w[2][u], 0x07030602u);
+        }
+    }
+    static __device__ __forceinline__ uint32_t widen_sel(uint32_t x, int t) {
+        return (t & 1) ? Mma<M>::template widen2<true>(x) : Mma<M>::template widen2<false>(x);
+    }
 
     // Head-dimension index of element i (< 8) of MFMA step s for lane group g.  Any
     // mapping works as long as K and Q use the same one; these keep every lane's 16-byte
@@ -673,22 +765,6 @@ struct MfmaSegment {
     static __device__ __forceinline__ uint4 widen8(uint32_t w0, uint32_t w1) {
         return uint4{Mma<M>::template widen2<false>(w0), Mma<M>::template widen2<true>(w0),
                      Mma<M>::template widen2<false>(w1), Mma<M>::template widen2<true>(w1)};
-    }
-
-    // One lane's V row piece (E elements) as E/2 words of operand-type pairs.
-    static __device__ __forceinline__ void v_halves(const VT& v, uint32_t* h) {
-        uint32_t w[VBYTES / 4];
-        words_of<VT>(v, w);
-        if constexpr (!kFp8) {
-#pragma unroll
-            for (int k = 0; k < E / 2; ++k) h[k] = w[k];
-        } else {
-#pragma unroll
-            for (int k = 0; k < E / 2; k += 2) {
-                h[k] = Mma<M>::template widen2<false>(w[k / 2]);
-                h[k + 1] = Mma<M>::template widen2<true>(w[k / 2]);
-            }
-        }
     }
 
     // Unit u of sequence b: head group u / qgroups (G = hpw heads of one KV head) and query
@@ -744,8 +820,21 @@ struct MfmaSegment {
                       __float_as_int(st[(4 * E + 2) * kWave]));
     }
 
+    // What a segment needs before it can issue its first block: the page-table chunk of
+    // block jb (lane i: the physical id of block jb + i; groups load theirs per run).  Loaded
+    // one segment ahead, so a new segment starts its loads without waiting on memory (its
+    // queries load alongside its first blocks).
+    struct Pre {
+        int tbl;
+    };
+    static __device__ __forceinline__ Pre prefetch(const DecodeParams& p, int lane, int b, int /*u*/, int jb) {
+        const int j = jb + lane;
+        return Pre{(!GROUPED && j < p.max_blocks) ? p.block_tables[(int64_t)b * p.max_blocks + j] : -1};
+    }
+
     static __device__ __forceinline__ void run(const DecodeParams& p, int lane, int b, int u, int jb, int je,
-                                               int jfirst, int nblk, int lo, int L, int64_t slot, bool defer) {
+                                               int jfirst, int nblk, int lo, int L, int64_t slot, bool defer,
+                                               const Pre& pre) {
         const int G = p.hpw;
         const int hg = u / p.qgroups;
         const int q0 = (u % p.qgroups) * p.qpw;        // first query of the unit
@@ -782,7 +871,7 @@ struct MfmaSegment {
             const int j = jbase + lane;
             return j < p.max_blocks ? table[j] : -1;
         };
-        int tbl = grouped ? 0 : table_chunk(jb);
+        int tbl = pre.tbl;
 
         // Q as the B operand: lane l holds Q[row c][dk(s, g) + i]; zero for rows past the unit.
         uint4 qb[KSTEPS];
@@ -808,7 +897,9 @@ struct MfmaSegment {
         // K arrives in whole rows (lane l: 16 bytes at 16 (l % KLPR) of row KTPL i + l / KLPR)
         // and is turned into the operand layout through this wave's LDS tile.
         const uint32_t kr_off = (uint32_t)((lane / KLPR) * tok_bytes + (int64_t)hk * D * EB) + 16 * (lane % KLPR);
-        __shared__ uint4 ktiles[kWaves][kBlockSize * KRS / 16];
+        // One tile per block of a pair.
+        constexpr int TILE = kBlockSize * KRS;
+        __shared__ uint4 ktiles[kWaves][2 * TILE / 16];
         char* ktile = (char*)ktiles[__builtin_amdgcn_readfirstlane(threadIdx.x / kWave)];
         char* kput = ktile + (lane / KLPR) * KRS + 16 * (lane % KLPR);
         const char* kget = ktile + c * KRS + 16 * g;
@@ -830,108 +921,156 @@ struct MfmaSegment {
             }
         }
 
-        auto issue = [&](int j, int jend, int jbase, Buf& bf) {
-            const int phys = live_block(p, tbl, j, jend, jbase);
-            const bool ok = phys >= 0;
-            const int64_t pb = ok ? phys : 0;
-            const auto rk = block_rsrc(kbase + pb * blk_bytes, ok ? (int)blk_bytes : 0);
-            const auto rv = block_rsrc(vbase + pb * blk_bytes, ok ? (int)blk_bytes : 0);
-            // K: KTPL whole rows per load.  V: rows 4g + i, E elements at E c.  Both are read
-            // once, in full lines, and streamed past the caches.
+        // Blocks j and j + 1 (K: KTPL whole rows per load.  V: rows 4g + i, E elements at E c.
+        // Both are read once, in full lines, and streamed past the caches.)
+        auto issue = [&](int j, int jend, int jbase, Pair& pr) {
 #pragma unroll
-            for (int i = 0; i < KLOADS; ++i) bf.k[i] = buffer_load16<kCacheStream>(rk, kr_off + (uint32_t)(i * KTPL * tok_bytes));
+            for (int q = 0; q < 2; ++q) {
+                Buf& bf = pr.b[q];
+                const int phys = live_block(p, tbl, j + q, jend, jbase);
+                const bool ok = phys >= 0;
+                const int64_t pb = ok ? phys : 0;
+                const auto rk = block_rsrc(kbase + pb * blk_bytes, ok ? (int)blk_bytes : 0);
+                const auto rv = block_rsrc(vbase + pb * blk_bytes, ok ? (int)blk_bytes : 0);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) bf.v[i] = load_v(rv, v_off + i * v_step);
-            if constexpr (kFp8) {
-                bf.ks = *(const float4*)(p.k_scale + pb * kBlockSize + 4 * g);
-                bf.vs = *(const float4*)(p.v_scale + pb * kBlockSize + 4 * g);
+                for (int i = 0; i < KLOADS; ++i)
+                    bf.k[i] = buffer_load16<kCacheStream>(rk, kr_off + (uint32_t)(i * KTPL * tok_bytes));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) bf.v[i] = load_v(rv, v_off + i * v_step);
+                if constexpr (kFp8) {
+                    bf.ks = *(const float4*)(p.k_scale + pb * kBlockSize + 4 * g);
+                    bf.vs = *(const float4*)(p.v_scale + pb * kBlockSize + 4 * g);
+                }
+                pr.ok[q] = ok;
             }
-            return ok;
+            return pr.ok[0] || pr.ok[1];
         };
 
-        auto consume = [&](int j, const Buf& bf0) {
-            Buf bf = bf0;
+        // the new token (row o of block jnew) comes from the inputs, not from its slot
+        auto patch_block = [&](Buf& bf) {
+            const bool krow = lane / KLPR == nt.o % KTPL;
+            const bool vrow = g == nt.o / 4;
+#pragma unroll
+            for (int i = 0; i < KLOADS; ++i)
+                if (i == nt.o / KTPL && krow) bf.k[i] = knew;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (i == nt.o % 4 && vrow) bf.v[i] = vnew;
+            if (h0 % (p.Hq / p.Hkv) == 0) {
+                if (krow) {
+                    char* kd = NewToken::slot_row((void*)p.key_cache, p, b, hk, D, nt.jnew, nt.o, 16 * (lane % KLPR));
+                    if (kd) *(uint4*)kd = knew;
+                }
+                if (vrow) {
+                    char* vd = NewToken::slot_row((void*)p.value_cache, p, b, hk, D, nt.jnew, nt.o, VBYTES * c);
+                    if (vd) *(VT*)vd = vnew;
+                }
+            }
+        };
+
+        auto consume = [&](int j, const Pair& pr0) {
+            Pair pr = pr0;
             if constexpr (APPEND) {
-                // the new token (row o of block jnew) comes from the inputs, not from its slot
-                if (patch && j == nt.jnew) {
-                    const bool krow = lane / KLPR == nt.o % KTPL;
-                    const bool vrow = g == nt.o / 4;
+                if (patch && j == nt.jnew) patch_block(pr.b[0]);
+                if (patch && j + 1 == nt.jnew) patch_block(pr.b[1]);
+            }
+            // K rows -> LDS -> A operand (lane l: 16 bytes of token c at byte 64 i + 16 g, i.e.
+            // 16-bit step s = i, or FP8 steps 2i and 2i + 1).  The tiles belong to this wave
+            // alone; the fences keep the compiler from moving these accesses past each other.
+            uint4 ka[2][KLOADS];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-                    for (int i = 0; i < KLOADS; ++i)
-                        if (i == nt.o / KTPL && krow) bf.k[i] = knew;
+            for (int q = 0; q < 2; ++q)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (i == nt.o % 4 && vrow) bf.v[i] = vnew;
-                    if (h0 % (p.Hq / p.Hkv) == 0) {
-                        if (krow) {
-                            char* kd = NewToken::slot_row((void*)p.key_cache, p, b, hk, D, nt.jnew, nt.o,
-                                                          16 * (lane % KLPR));
-                            if (kd) *(uint4*)kd = knew;
-                        }
-                        if (vrow) {
-                            char* vd = NewToken::slot_row((void*)p.value_cache, p, b, hk, D, nt.jnew, nt.o, VBYTES * c);
-                            if (vd) *(VT*)vd = vnew;
-                        }
+                for (int i = 0; i < KLOADS; ++i) *(uint4*)(kput + q * TILE + i * KTPL * KRS) = pr.b[q].k[i];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int i = 0; i < KLOADS; ++i) ka[q][i] = *(const uint4*)(kget + q * TILE + 64 * i);
+
+            // S^T for each block's 16 tokens x 16 head rows (lane l: tokens 4g + r of head c).
+            f32x4_t S[2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                S[q] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+                if constexpr (!kFp8) {
+#pragma unroll
+                    for (int s = 0; s < KSTEPS; ++s) S[q] = Mma<M>::k32(ka[q][s], qb[s], S[q]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < KLOADS; ++i) {
+                        S[q] = Mma<M>::k32(widen8(ka[q][i].x, ka[q][i].y), qb[2 * i], S[q]);
+                        S[q] = Mma<M>::k32(widen8(ka[q][i].z, ka[q][i].w), qb[2 * i + 1], S[q]);
                     }
                 }
             }
-            // K rows -> LDS -> A operand (lane l: 16 bytes of token c at byte 64 i + 16 g, i.e.
-            // 16-bit step s = i, or FP8 steps 2i and 2i + 1).  The tile belongs to this wave
-            // alone; the fences keep the compiler from moving these accesses past each other.
-            uint4 ka[KLOADS];
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // Score i < 8: token 4g + i % 4 of block i / 4.
+            float f[8];
 #pragma unroll
-            for (int i = 0; i < KLOADS; ++i) *(uint4*)(kput + i * KTPL * KRS) = bf.k[i];
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            for (int q = 0; q < 2; ++q) {
+                const float ksc[4] = {pr.b[q].ks.x, pr.b[q].ks.y, pr.b[q].ks.z, pr.b[q].ks.w};
 #pragma unroll
-            for (int i = 0; i < KLOADS; ++i) ka[i] = *(const uint4*)(kget + 64 * i);
-
-            // S^T for the block's 16 tokens x 16 head rows (lane l: tokens 4g + r of head c).
-            f32x4_t S = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-            if constexpr (!kFp8) {
+                for (int r = 0; r < 4; ++r) f[4 * q + r] = kFp8 ? p.scale_log2 * ksc[r] : p.scale_log2;
+            }
+            // This lane's row attends to tokens [lo, hs).  The common case takes one test per
+            // pair: both blocks hold data throughout and every row sees all of the pair or none
+            // of it.  Otherwise, per token, valid: it holds data this unit reads (V rows of other
+            // tokens select zeros); seen: this lane's row attends to it.
+            const int j16 = j * kBlockSize;
+            const int hs = run_on ? min(rowL, last + 1) : lo;
+            const bool fast = pr.ok[0] && pr.ok[1] && j16 >= lo && j16 + 2 * kBlockSize <= run_lv &&
+                              !__ballot(hs > j16 && hs < j16 + 2 * kBlockSize);
+            float sc[8];
+            bool valid[8], seen[8];
+            if (fast) {
+                const bool on = hs > j16;
 #pragma unroll
-                for (int s = 0; s < KSTEPS; ++s) S = Mma<M>::k32(ka[s], qb[s], S);
+                for (int i = 0; i < 8; ++i) sc[i] = on ? S[i / 4][i % 4] * f[i] : kNegInf;
             } else {
 #pragma unroll
-                for (int i = 0; i < KLOADS; ++i) {
-                    S = Mma<M>::k32(widen8(ka[i].x, ka[i].y), qb[2 * i], S);
-                    S = Mma<M>::k32(widen8(ka[i].z, ka[i].w), qb[2 * i + 1], S);
+                for (int i = 0; i < 8; ++i) {
+                    const int t = j16 + kBlockSize * (i / 4) + 4 * g + i % 4;
+                    valid[i] = pr.ok[i / 4] && t >= lo && t < run_lv;
+                    seen[i] = valid[i] && run_on && t < rowL && t <= last;
+                    sc[i] = seen[i] ? S[i / 4][i % 4] * f[i] : kNegInf;
                 }
             }
-            const float ksc[4] = {bf.ks.x, bf.ks.y, bf.ks.z, bf.ks.w};
-            const float vsc[4] = {bf.vs.x, bf.vs.y, bf.vs.z, bf.vs.w};
-            // valid: the token holds data this unit reads (V rows of other tokens select zeros);
-            // seen: this lane's row attends to it (its query's causal limit).
-            float sc[4];
-            bool valid[4], seen[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = j * kBlockSize + 4 * g + r;
-                valid[r] = t >= lo && t < run_lv;
-                seen[r] = run_on && t >= lo && t < rowL && t <= last;
-                const float f = kFp8 ? p.scale_log2 * ksc[r] : p.scale_log2;
-                sc[r] = seen[r] ? S[r] * f : kNegInf;
-            }
-            // Block maximum of head c over the four lane groups.  The reference m moves only
-            // when the block exceeds it by more than kSlack (or on the first scores), so the
-            // exponentials stay <= 2^kSlack and most blocks skip the output rescale; any
+            // Pair maximum of head c over the four lane groups.  The reference m moves only
+            // when the pair exceeds it by more than kSlack (or on the first scores), so the
+            // exponentials stay <= 2^kSlack and most pairs skip the output rescale; any
             // reference gives the same softmax, this one keeps the arithmetic in range.
-            const float mb = group_max(__builtin_fmaxf(__builtin_fmaxf(sc[0], sc[1]), __builtin_fmaxf(sc[2], sc[3])));
+            float mx = sc[0];
+#pragma unroll
+            for (int i = 1; i < 8; ++i) mx = __builtin_fmaxf(mx, sc[i]);
+            const float mb = group_max(mx);
             const float mn = (mb > m + kSlack) ? mb : m;
             const float ms = (mn == kNegInf) ? 0.0f : mn;
             const float alpha = fast_exp2(m - ms);
             m = mn;
-            float pr[4];
+            float pw[8];
             float psum = 0.0f;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                pr[r] = fast_exp2(sc[r] - ms);
-                psum += pr[r];
-                if constexpr (kFp8) pr[r] = seen[r] ? pr[r] * vsc[r] : 0.0f;
+            for (int i = 0; i < 8; ++i) {
+                pw[i] = fast_exp2(sc[i] - ms);
+                psum += pw[i];
+            }
+            if constexpr (kFp8) {
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const float vsc[4] = {pr.b[q].vs.x, pr.b[q].vs.y, pr.b[q].vs.z, pr.b[q].vs.w};
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = 4 * q + r;
+                        // (unwritten slots may hold any scale, even NaN: only seen tokens are scaled)
+                        if (fast) pw[i] *= vsc[r];
+                        else pw[i] = seen[i] ? pw[i] * vsc[r] : 0.0f;
+                    }
+                }
             }
             lsum = lsum * alpha + psum;
             // Rescale the output rows 4g + r when some running max moved.
@@ -944,37 +1083,55 @@ struct MfmaSegment {
                 }
             }
 
-            // V rows 4g + i as operand-type pairs; rows past the context select zeros (P is
-            // zero there, and 0 * NaN would not be).
-            uint32_t vh[4][E / 2];
+            // P = hi + lo in the operand type (A operand: head c, k = 8g + i).
+            uint32_t ph[4], pl[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                v_halves(bf.v[i], vh[i]);
-#pragma unroll
-                for (int k = 0; k < E / 2; ++k) vh[i][k] = valid[i] ? vh[i][k] : 0u;
+            for (int k = 0; k < 4; ++k) {
+                ph[k] = Mma<M>::pack_rtz(pw[2 * k], pw[2 * k + 1]);
+                const float2_t fh = unpack2(M{}, ph[k]);
+                pl[k] = Mma<M>::pack_rtz(pw[2 * k] - fh.x, pw[2 * k + 1] - fh.y);
             }
+            const uint4 a_hi = uint4{ph[0], ph[1], ph[2], ph[3]};
+            const uint4 a_lo = uint4{pl[0], pl[1], pl[2], pl[3]};
 
-            // P = hi + lo in the operand type (A operand: head c, rows 4g..4g+3).
-            const uint32_t h01 = Mma<M>::pack_rtz(pr[0], pr[1]);
-            const uint32_t h23 = Mma<M>::pack_rtz(pr[2], pr[3]);
-            const float2_t f01 = unpack2(M{}, h01);
-            const float2_t f23 = unpack2(M{}, h23);
-            const uint2 a_hi = uint2{h01, h23};
-            const uint2 a_lo = uint2{Mma<M>::pack_rtz(pr[0] - f01.x, pr[1] - f01.y),
-                                     Mma<M>::pack_rtz(pr[2] - f23.x, pr[3] - f23.y)};
+            // V of both blocks as B operands; rows past the data select zeros (P is zero there,
+            // and 0 * NaN would not be).
+            constexpr int VW = (VBYTES + 3) / 4;     // words per row piece
+            uint32_t w[2][4][VW];
 #pragma unroll
-            for (int t = 0; t < E; ++t) {
-                const int k = t >> 1;
-                uint2 bt;
-                if (t & 1) {
-                    bt.x = (vh[0][k] >> 16) | (vh[1][k] & 0xFFFF0000u);
-                    bt.y = (vh[2][k] >> 16) | (vh[3][k] & 0xFFFF0000u);
-                } else {
-                    bt.x = (vh[0][k] & 0xFFFFu) | (vh[1][k] << 16);
-                    bt.y = (vh[2][k] & 0xFFFFu) | (vh[3][k] << 16);
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) words_of<VT>(pr.b[q].v[i], w[q][i]);
+            if (!fast) {
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int u = 0; u < VW; ++u) w[q][i][u] = valid[4 * q + i] ? w[q][i][u] : 0u;
+            }
+            if constexpr (!kFp8) {
+                static_assert(VW == E / 2, "16-bit rows: two elements per word");
+#pragma unroll
+                for (int t = 0; t < E; ++t) {
+                    const uint2 b0 = v_tile16(w[0], t);
+                    const uint2 b1 = v_tile16(w[1], t);
+                    const uint4 bt = uint4{b0.x, b0.y, b1.x, b1.y};
+                    O[t] = Mma<M>::k32(a_hi, bt, O[t]);
+                    O[t] = Mma<M>::k32(a_lo, bt, O[t]);
                 }
-                O[t] = Mma<M>::k16(a_hi, bt, O[t]);
-                O[t] = Mma<M>::k16(a_lo, bt, O[t]);
+            } else {
+                uint32_t x01[2][VW][2], x23[2][VW][2];
+                v_codes(w[0], x01[0], x23[0]);
+                v_codes(w[1], x01[1], x23[1]);
+#pragma unroll
+                for (int t = 0; t < E; ++t) {
+                    const int u = t / 4, h = (t % 4) / 2;
+                    const uint4 bt = uint4{widen_sel(x01[0][u][h], t), widen_sel(x23[0][u][h], t),
+                                           widen_sel(x01[1][u][h], t), widen_sel(x23[1][u][h], t)};
+                    O[t] = Mma<M>::k32(a_hi, bt, O[t]);
+                    O[t] = Mma<M>::k32(a_lo, bt, O[t]);
+                }
             }
         };
 
@@ -1016,7 +1173,7 @@ struct MfmaSegment {
                 }
                 tbl = table_chunk(j0);
             }
-            stream_blocks<NB, Buf>(j0, j1, tbl, table_chunk, issue, consume);
+            stream_blocks<NB, 2, Pair>(j0, j1, tbl, table_chunk, issue, consume);
             o += j1 - j0;
         }
 
@@ -1090,40 +1247,60 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeParams p) 
         const int jb = j0 + part * p.part_blocks;
         if (jb >= nblk && !(part == 0 && nblk == 0)) return;   // L == 0: partition 0 writes zeros
         const int je = min(nblk, jb + p.part_blocks);
-        Segment::run(p, lane, b, hg, jb, je, j0, nblk, lo, L, (int64_t)s * p.NP + part, false);
+        Segment::run(p, lane, b, hg, jb, je, j0, nblk, lo, L, (int64_t)s * p.NP + part, false,
+                     Segment::prefetch(p, lane, b, hg, jb));
         return;
     }
 
     // Balanced split: head group hg of the range of team `team` in the (sequence, block) order.
     const int team = w / p.groups;
     const int hg = w % p.groups;
-    const SeqTable st = seq_table(p, lane);
-    const Ranges rg = make_ranges(p, st.total);
+    Cursor cur = cursor_chunk(p, lane, 0, 0);
+    const Ranges rg = make_ranges(p, num_entries(p) <= kWave ? cur.end : total_blocks(p, lane));
     int pos = rg.begin(team);
     const int pos_end = rg.end(team);
     const int64_t slot_base = (int64_t)hg * (p.teams + num_entries(p)) + team;
     int64_t deferred = -1;   // workspace slot of a stashed partial
-    while (pos < pos_end) {
+    // The range's segments in order; each one's table chunk and queries are loaded while the
+    // one before it runs.
+    auto next = [&](SegInfo& si) -> bool {
+        if (pos >= pos_end) return false;
         // Position offsets count the blocks in play of the sequence, which start at logical
-        // block j0.
-        const SeqPos sp = locate(p, st, lane, pos);
-        const int off = pos - sp.start;
+        // block jfirst.
+        int len;
+        const SeqPos sp = cursor_find(p, lane, cur, pos, len);
         // entry sp.b: a sequence, or the group of sequences sp.b * sgroup .. (whose segment
         // resolves its own lengths)
-        const int b = p.sgroup > 0 ? sp.b * p.sgroup : sp.b;
-        const int L = p.sgroup > 0 ? 0 : seq_len(p, sp.b);
-        const int lo = first_token(p, L);
-        const int j0 = lo / kBlockSize;
-        const int jb = j0 + off;
-        const int je = min(j0 + sp.nblk, jb + (pos_end - pos));
-        const int64_t slot = slot_base + sp.b;
+        si.b = p.sgroup > 0 ? sp.b * p.sgroup : sp.b;
+        si.L = len;
+        si.lo = first_token(p, len);
+        si.jfirst = si.lo / kBlockSize;
+        si.nblk = si.jfirst + sp.nblk;
+        si.jb = si.jfirst + (pos - sp.start);
+        si.je = min(si.nblk, si.jb + (pos_end - pos));
+        si.slot = slot_base + sp.b;
         // Only a wave's first segment can end unfinished before its last one; its partial
         // is written after the last segment (see the segment's stash).
-        const bool last = pos + (je - jb) >= pos_end;
-        const bool whole = jb == j0 && je == j0 + sp.nblk;
-        Segment::run(p, lane, b, hg, jb, je, j0, j0 + sp.nblk, lo, L, slot, !last);
-        if (!last && !whole) deferred = slot;
-        pos += je - jb;
+        const bool last = pos + (si.je - si.jb) >= pos_end;
+        const bool whole = si.jb == si.jfirst && si.je == si.nblk;
+        si.defer = !last;
+        if (!last && !whole) deferred = si.slot;
+        pos += si.je - si.jb;
+        return true;
+    };
+    SegInfo si;
+    bool has = next(si);
+    typename Segment::Pre pre;
+    if (has) pre = Segment::prefetch(p, lane, si.b, hg, si.jb);
+    while (has) {
+        SegInfo sn;
+        const bool has_n = next(sn);
+        typename Segment::Pre pre_n;
+        if (has_n) pre_n = Segment::prefetch(p, lane, sn.b, hg, sn.jb);
+        Segment::run(p, lane, si.b, hg, si.jb, si.je, si.jfirst, si.nblk, si.lo, si.L, si.slot, si.defer, pre);
+        si = sn;
+        pre = pre_n;
+        has = has_n;
     }
     if (deferred >= 0) Segment::flush(p, lane, deferred);
 }
