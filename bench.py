@@ -226,6 +226,9 @@ def time_workload(name, steps, warmup, replicas, sample=None, partition_size=Non
     torch.cuda.synchronize()
     dec_ms = sorted(e[0].elapsed_time(e[1]) for e in events)
     n = len(dec_ms)
+    kind = ("fused" if fused else f"q_len {q_len}" if q_len > 1 else "shared prefix" if shared_prefix
+            else f"window {window}" if window > 0 else "append + decode")
+    print(f"[bench] {name} ({kind}): {step_gpu_ms * 1e3:.1f} us per step", file=sys.stderr, flush=True)
     return {
         "w": w,
         "cpu_sample": host,
@@ -264,12 +267,12 @@ def read_ceiling(steps=50, warmup=5):
     stream: a plain streaming read of a 2 GiB buffer.  paged_gather: the llama7b decode's
     access pattern without the attention (every head's 256-byte rows of 16-token blocks of 32
     KV heads, blocks in random order, next block's loads in flight) in the decode's order
-    (teams of one wave per KV head reading the same blocks; 1024 waves, the decode's count for
-    a 16-bit cache), 4400 blocks (577 MB) per launch; paged_gather_head_major: the same rows
+    (teams of one wave per KV head reading the same blocks; 1024 waves, the decode's count),
+    4400 blocks (577 MB) per launch; paged_gather_head_major: the same rows
     with each wave reading one head of consecutive blocks (2048 waves).
     paged_gather_by_workload: the team-order probe in the geometry of the gqa70b (8 KV heads,
-    256-byte rows, 1024 waves) and fp8beams (8 KV heads, 128-byte rows of one-byte codes, 2048
-    waves) workloads, over as many block reads as the workload's K and V pools hold unique
+    256-byte rows) and fp8beams (8 KV heads, 128-byte rows of one-byte codes) workloads at 1024
+    waves, over as many block reads as the workload's K and V pools hold unique
     blocks (the FP8 scales aside).  Each launch takes its blocks from one of three disjoint
     sets of a 2 GiB pool.  Probe kernels of libpaprobe.so
     (paged_kv_cache_187_amd/probe/pa_probe.hip), timed with HIP events.
@@ -323,7 +326,7 @@ def read_ceiling(steps=50, warmup=5):
            "paged_gather": gather(32, 256, 4400, 1024),
            "paged_gather_head_major": gather(32, 256, 4400, 2048, teams=False),
            "paged_gather_by_workload": {"gqa70b": gather(8, 256, 2 * unique_blocks("gqa70b"), 1024),
-                                        "fp8beams": gather(8, 128, 2 * unique_blocks("fp8beams"), 2048)}}
+                                        "fp8beams": gather(8, 128, 2 * unique_blocks("fp8beams"), 1024)}}
     del buf
     torch.cuda.empty_cache()
     return res
@@ -623,6 +626,8 @@ def main():
     ap.add_argument("--unfused", action="store_true",
                     help="time the step as pa_append_kv + pa_decode instead of pa_decode_append (one call); "
                          "the default run also reports the unfused step of the main workload")
+    ap.add_argument("--no-unfused-line", action="store_true",
+                    help="skip the unfused step of the main workload (counter runs of the fused step alone)")
     ap.add_argument("--partition-size", type=int, default=None,
                     help="override the workload's partition length (tokens; 0 = library's choice)")
     args = ap.parse_args()
@@ -689,7 +694,7 @@ def main():
             del r
             torch.cuda.empty_cache()
 
-    if fused:
+    if fused and not args.no_unfused_line:
         r = time_workload(args.workload, args.steps, args.warmup, args.replicas, partition_size=args.partition_size,
                           use_graphs=args.graphs)
         also[f"{args.workload}_unfused"] = summarize(args.workload, r)
