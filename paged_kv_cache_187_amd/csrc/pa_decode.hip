@@ -1253,8 +1253,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeParams p) 
     }
 
     // Balanced split: head group hg of the range of team `team` in the (sequence, block) order.
-    const int team = w / p.groups;
-    const int hg = w % p.groups;
+    // Workgroups go to the eight XCDs in turn (workgroup i on XCD i % 8); the waves are
+    // renumbered so that each XCD holds one contiguous stretch of teams, i.e. neighbouring
+    // positions (the beams of one prompt, whose shared blocks then meet in one L2).
+    int wl = w;
+    if (gridDim.x % 8 == 0 && p.num_waves == (int)gridDim.x * kWaves) {   // a permutation of the waves
+        const int i = blockIdx.x;
+        wl = ((i % 8) * (int)(gridDim.x / 8) + i / 8) * kWaves + (w - i * kWaves);
+    }
+    const int team = wl / p.groups;
+    const int hg = wl % p.groups;
     Cursor cur = cursor_chunk(p, lane, 0, 0);
     const Ranges rg = make_ranges(p, num_entries(p) <= kWave ? cur.end : total_blocks(p, lane));
     int pos = rg.begin(team);
