@@ -275,7 +275,8 @@ def read_ceiling(steps=50, warmup=5):
     waves, over as many block reads as the workload's K and V pools hold unique
     blocks (the FP8 scales aside).  Each launch takes its blocks from one of three disjoint
     sets of a 2 GiB pool.  Probe kernels of libpaprobe.so
-    (paged_kv_cache_187_amd/probe/pa_probe.hip), timed with HIP events.
+    (paged_kv_cache_187_amd/probe/pa_probe.hip), timed as the decode step is: one HIP event
+    pair around `steps` back-to-back launches.
     """
     import ctypes
     import torch
@@ -294,15 +295,17 @@ def read_ceiling(steps=50, warmup=5):
     g = torch.Generator().manual_seed(7)
 
     def run(launch, n):
+        # timed like the decode step: one event pair around n back-to-back launches (events
+        # between launches would add their own packets to every launch)
         for i in range(warmup):
             assert launch(i) == 0
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
         for i in range(n):
-            ev[i][0].record(stream)
             assert launch(warmup + i) == 0
-            ev[i][1].record(stream)
+        b.record(stream)
         torch.cuda.synchronize()
-        return sorted(a.elapsed_time(b) for a, b in ev)[n // 2] * 1e-3
+        return a.elapsed_time(b) * 1e-3 / n
 
     def gather(hkv, row, n_ids, waves, teams=True):
         blk = 16 * hkv * row
