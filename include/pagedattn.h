@@ -192,8 +192,7 @@ int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_heads, int32_t nu
  * arguments, whatever the cache dtype ((size_t)-1 for invalid arguments; 0
  * when nothing is split, i.e. fixed partitions with max_context_len <=
  * partition_size).  The balanced split runs 1024 waves, or 2048 for an FP8 cache
- * whose head groups stay off the matrix cores (num_heads / num_kv_heads of 1 or 2,
- * or above 16 and not a multiple of 16); the size returned is the larger one's.  The
+ * (shared-prefix groups: 1024 always); the size returned is the larger one's.  The
  * workspace holds float32 partial results: per (slot, head of the group) a
  * V sum of head_dim floats, followed by all (max, sum of exponentials)
  * pairs.  Its contents need no initialisation and are scratch after the call;

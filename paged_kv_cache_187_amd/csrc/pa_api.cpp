@@ -16,12 +16,15 @@ namespace {
 
 constexpr int32_t kMaxPartition = 1 << 20;
 constexpr int64_t kMaxWork = ((int64_t)1 << 30);  // waves, or (head group, block) pairs, per launch
-// Waves of the balanced split.  One wave per SIMD keeps the memory system saturated (the
-// matrix-core path streams two blocks per ring entry); on the VALU path an FP8 block
-// needs two waves per SIMD to overlap its conversions with the loads.  Workspace queries
-// size for the larger count (an upper bound).
-constexpr int64_t kBalancedWaves = 1024;            // 4 per CU
-constexpr int64_t kBalancedWavesValuFp8 = 2048;     // 8 per CU
+// Waves of the balanced split.  One wave per SIMD keeps the memory system saturated for
+// 16-bit caches (the matrix-core path streams two blocks per ring entry).  An FP8 block
+// carries half the bytes for about the same work per block, so FP8 caches run two waves
+// per SIMD, one wave's conversions and matrix products overlapping the other's loads;
+// shared-prefix groups stay at one wave per SIMD (twice the ranges would double their
+// 16-row partials and per-range start-up).  Workspace queries size for the larger count
+// (an upper bound).
+constexpr int64_t kBalancedWaves = 1024;       // 4 per CU
+constexpr int64_t kBalancedWavesFp8 = 2048;    // 8 per CU
 constexpr int32_t kMaxQueries = 4096;               // new tokens per sequence in one multi-query call
 
 // Launch shape shared by pa_decode and pa_decode_workspace_bytes.
@@ -72,7 +75,7 @@ Plan make_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_
         // Teams of one wave per head group share a range of (sequence, block) positions:
         // about balanced_waves waves, at most one team per block and at least one team.
         const int64_t blocks = entries * max_blocks;   // upper bound of (entry, block) positions
-        const int64_t balanced_waves = fp8 && !pl.mfma ? kBalancedWavesValuFp8 : kBalancedWaves;
+        const int64_t balanced_waves = fp8 && seq_group == 0 ? kBalancedWavesFp8 : kBalancedWaves;
         int64_t teams = balanced_waves / pl.groups;
         if (teams > blocks) teams = blocks;
         if (teams < 1) teams = 1;

@@ -153,32 +153,6 @@ __device__ SeqTable seq_table(const DecodeParams& p, int lane) {
     return st;
 }
 
-// The non-empty entry holding balanced-order position pos, where the position of block j
-// of entry b is start_b + j and 0 <= pos < total_blocks.
-__device__ SeqPos locate(const DecodeParams& p, const SeqTable& st, int lane, int pos) {
-    if (st.single) {
-        const uint64_t mask = __ballot(st.nb > 0 && st.start <= pos);
-        const int lb = 63 - __builtin_clzll(mask);
-        return {lb, __builtin_amdgcn_readlane(st.start, lb), __builtin_amdgcn_readlane(st.nb, lb)};
-    }
-    const int n = num_entries(p);
-    int carry = 0;
-    for (int c = 0; c < n; c += kWave) {
-        const int b = c + lane;
-        const int nb = b < n ? entry_blocks(p, b) : 0;
-        const int incl = wave_incl_scan(nb, lane);
-        const int start = carry + incl - nb;
-        const uint64_t mask = __ballot(nb > 0 && start <= pos);
-        const int chunk_total = __builtin_amdgcn_readlane(incl, kWave - 1);
-        if (carry + chunk_total > pos) {
-            const int lb = 63 - __builtin_clzll(mask);
-            return {c + lb, __builtin_amdgcn_readlane(start, lb), __builtin_amdgcn_readlane(nb, lb)};
-        }
-        carry += chunk_total;
-    }
-    return {0, 0, 0};
-}
-
 // A wave's walk through the balanced order.  The lanes hold 64 consecutive entries
 // c .. c + 63: entry c + lane's clamped length (sequences; 0 for groups, whose segments
 // read their own lengths), block count and first position.  Positions only grow along a
@@ -365,6 +339,7 @@ struct NewToken {
 // consecutive heads per slot).
 template <typename QT, typename CT, int D, int HPW, int NB, bool APPEND>
 struct ValuSegment {
+static constexpr int kWavesPerSimd = 1;   // no bound beyond the launch bounds
 struct Buf {
     uint4 k[Layout<CT, D>::LPB], v[Layout<CT, D>::LPB];
     float ks[Layout<CT, D>::LPB], vs[Layout<CT, D>::LPB];
@@ -705,6 +680,9 @@ struct MfmaSegment {
     using M = QT;
     static constexpr int EB = Storage<CT>::bytes;
     static constexpr bool kFp8 = EB == 1;
+    // FP8 units run two waves per SIMD (the host launches twice the waves outside
+    // shared-prefix groups), so their registers must fit in half the file.
+    static constexpr int kWavesPerSimd = kFp8 ? 2 : 1;
     static constexpr int KSTEPS = D / 32;          // 16x16x32 steps over the head dimension
     static constexpr int E = D / 16;               // head-dim elements per lane per V row = tiles
     static constexpr int KLOADS = kFp8 ? KSTEPS / 2 : KSTEPS;   // 16-byte K loads per lane per block
@@ -715,10 +693,12 @@ struct MfmaSegment {
     static_assert(KTPL * KLOADS == kBlockSize, "whole-row K loads cover the block");
     using VT = typename Bytes<VBYTES>::T;
 
+    // FP8 scales: lane (g, c) holds the scale of token 4g + c % 4; each lane of a quad takes
+    // the four of its lane group from the quad (quad_scale).
     struct Buf {
         uint4 k[KLOADS];
         VT v[4];
-        float4 ks, vs;
+        float ks, vs;
     };
     // The ring holds blocks in pairs: the P V product runs on 16x16x32 tiles, whose 32-deep
     // contraction covers two blocks (k = 8 g + i is token 4 g + i % 4 of block i / 4; the
@@ -749,6 +729,10 @@ struct MfmaSegment {
             x23[u][0] = __builtin_amdgcn_perm(w[3][u], w[2][u], 0x05010400u);
             x23[u][1] = __builtin_amdgcn_perm(w[3][u], w[2][u], 0x07030602u);
         }
+    }
+    template <int R>
+    static __device__ __forceinline__ float quad_scale(float x) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), R * 0x55, 0xF, 0xF, false));
     }
     static __device__ __forceinline__ uint32_t widen_sel(uint32_t x, int t) {
         return (t & 1) ? Mma<M>::template widen2<true>(x) : Mma<M>::template widen2<false>(x);
@@ -938,8 +922,8 @@ struct MfmaSegment {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) bf.v[i] = load_v(rv, v_off + i * v_step);
                 if constexpr (kFp8) {
-                    bf.ks = *(const float4*)(p.k_scale + pb * kBlockSize + 4 * g);
-                    bf.vs = *(const float4*)(p.v_scale + pb * kBlockSize + 4 * g);
+                    bf.ks = p.k_scale[pb * kBlockSize + 4 * g + (lane & 3)];
+                    bf.vs = p.v_scale[pb * kBlockSize + 4 * g + (lane & 3)];
                 }
                 pr.ok[q] = ok;
             }
@@ -1013,7 +997,8 @@ struct MfmaSegment {
             float f[8];
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
-                const float ksc[4] = {pr.b[q].ks.x, pr.b[q].ks.y, pr.b[q].ks.z, pr.b[q].ks.w};
+                const float ksc[4] = {quad_scale<0>(pr.b[q].ks), quad_scale<1>(pr.b[q].ks),
+                                      quad_scale<2>(pr.b[q].ks), quad_scale<3>(pr.b[q].ks)};
 #pragma unroll
                 for (int r = 0; r < 4; ++r) f[4 * q + r] = kFp8 ? p.scale_log2 * ksc[r] : p.scale_log2;
             }
@@ -1062,7 +1047,8 @@ struct MfmaSegment {
             if constexpr (kFp8) {
 #pragma unroll
                 for (int q = 0; q < 2; ++q) {
-                    const float vsc[4] = {pr.b[q].vs.x, pr.b[q].vs.y, pr.b[q].vs.z, pr.b[q].vs.w};
+                    const float vsc[4] = {quad_scale<0>(pr.b[q].vs), quad_scale<1>(pr.b[q].vs),
+                                          quad_scale<2>(pr.b[q].vs), quad_scale<3>(pr.b[q].vs)};
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int i = 4 * q + r;
@@ -1227,7 +1213,8 @@ struct MfmaSegment {
 
 
 template <typename Segment>
-__global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Segment::kWavesPerSimd)))
+void decode_kernel(const DecodeParams p) {
     const int lane = threadIdx.x & (kWave - 1);
     const int w = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     if (w >= p.num_waves) return;

@@ -65,8 +65,8 @@ def test_partition_and_workspace_sizes(lib):
     assert pa.decode_workspace_bytes(8, 32, 32, 128, 131072, 512) == 8 * 32 * 256 * 130 * 4
     assert pa.decode_workspace_bytes(4, 4, 4, 64, 50, 512) == 0               # one partition: none
     # balanced: one slot per wave plus one per (sequence, head group).  GQA group of 8 heads
-    # per wave on the matrix cores: 1024 waves (64 sequences x 8 groups)
-    assert pa.decode_workspace_bytes(64, 64, 8, 128, 4096, 0) == (1024 + 64 * 8) * 8 * 130 * 4
+    # per wave on the matrix cores, sized for the FP8 cache's 2048 waves (+ 64 sequences x 8 groups)
+    assert pa.decode_workspace_bytes(64, 64, 8, 128, 4096, 0) == (2048 + 64 * 8) * 8 * 130 * 4
     # MHA on the VALU path: sized for the FP8 cache's 2048 waves (64 teams x 32 heads)
     assert pa.decode_workspace_bytes(8, 32, 32, 128, 131072, 0) == 32 * (64 + 8) * 130 * 4
     # little work: one wave per (head group, block) pair at most
@@ -102,7 +102,7 @@ def test_multi_query_workspace_and_checks(lib):
 def test_shared_prefix_workspace_and_checks(lib):
     bad = ctypes.c_size_t(-1).value
     # 16 groups of 4 sequences, group of 4 heads: units = 16 groups x 8 KV heads, 16 rows each;
-    # slots = 1024 waves (matrix cores) + 128 units
+    # slots = 1024 waves (matrix cores; groups run one wave per SIMD) + 128 units
     assert lib.pa_decode_shared_prefix_workspace_bytes(64, 4, 32, 8, 128, 1280) == (1024 + 128) * 16 * 130 * 4
     # little work: 2 groups x 2 KV heads = 4 units of at most 2 sequences x 2 blocks: 16 waves,
     # slots = 16 + 4, rows = 2 sequences x 2 heads
