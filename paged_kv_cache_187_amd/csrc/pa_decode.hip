@@ -207,8 +207,8 @@ __device__ SeqPos seq_entry(const DecodeParams& p, const SeqTable& st, int lane,
 
 // Ranges of the balanced split: the T block positions are cut into n <= teams ranges
 // whose lengths differ by at most one (range r is [floor(r T / n), floor((r + 1) T / n))),
-// range r running on team r (waves r * groups .. r * groups + groups - 1, one per head
-// group).  Range boundaries depend only on the lengths and the launch shape.  The partial
+// each running on one team of `groups` waves, one per head group (team r when there are as
+// many ranges as teams).  Range boundaries depend only on the lengths and the launch shape.  The partial
 // of entry e, head group hg from range r goes to workspace slot hg * (teams + entries) +
 // r + e: for one head group, r + e is unique because ranges and entries both advance with
 // the position, and the slots of one (entry, head group) are consecutive in r, i.e. in
@@ -1252,9 +1252,15 @@ void decode_kernel(const DecodeParams p) {
     const int hg = wl % p.groups;
     Cursor cur = cursor_chunk(p, lane, 0, 0);
     const Ranges rg = make_ranges(p, num_entries(p) <= kWave ? cur.end : total_blocks(p, lane));
-    int pos = rg.begin(team);
-    const int pos_end = rg.end(team);
-    const int64_t slot_base = (int64_t)hg * (p.teams + num_entries(p)) + team;
+    // With fewer ranges than teams (little work, or the shared-prefix groups' minimum range
+    // length) the ranges go to evenly spaced teams, so the idle teams spread over the XCDs:
+    // team t runs range floor((t + 1) n / teams) - 1 when that differs from its predecessor's.
+    const int r_next = (int)((int64_t)(team + 1) * rg.n / p.teams);
+    if (r_next == (int)((int64_t)team * rg.n / p.teams)) return;
+    const int r = r_next - 1;
+    int pos = rg.begin(r);
+    const int pos_end = rg.end(r);
+    const int64_t slot_base = (int64_t)hg * (p.teams + num_entries(p)) + r;
     int64_t deferred = -1;   // workspace slot of a stashed partial
     // The range's segments in order; each one's table chunk and queries are loaded while the
     // one before it runs.
