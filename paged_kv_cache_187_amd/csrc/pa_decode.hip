@@ -730,9 +730,10 @@ struct MfmaSegment {
             x23[u][1] = __builtin_amdgcn_perm(w[3][u], w[2][u], 0x07030602u);
         }
     }
+    // (a plain DPP move, which the compiler folds into the multiply that uses it)
     template <int R>
     static __device__ __forceinline__ float quad_scale(float x) {
-        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), R * 0x55, 0xF, 0xF, false));
+        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), R * 0x55, 0xF, 0xF, true));
     }
     static __device__ __forceinline__ uint32_t widen_sel(uint32_t x, int t) {
         return (t & 1) ? Mma<M>::template widen2<true>(x) : Mma<M>::template widen2<false>(x);
@@ -993,15 +994,21 @@ struct MfmaSegment {
                     }
                 }
             }
-            // Score i < 8: token 4g + i % 4 of block i / 4.
+            // Score i < 8: token 4g + i % 4 of block i / 4, times the softmax scale (FP8: and the
+            // token's K scale, this lane's one multiplied in before the quad shares them).
             float f[8];
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
-                const float ksc[4] = {quad_scale<0>(pr.b[q].ks), quad_scale<1>(pr.b[q].ks),
-                                      quad_scale<2>(pr.b[q].ks), quad_scale<3>(pr.b[q].ks)};
-#pragma unroll
-                for (int r = 0; r < 4; ++r) f[4 * q + r] = kFp8 ? p.scale_log2 * ksc[r] : p.scale_log2;
+                const float kl = kFp8 ? p.scale_log2 * pr.b[q].ks : p.scale_log2;
+                f[4 * q + 0] = kFp8 ? quad_scale<0>(kl) : kl;
+                f[4 * q + 1] = kFp8 ? quad_scale<1>(kl) : kl;
+                f[4 * q + 2] = kFp8 ? quad_scale<2>(kl) : kl;
+                f[4 * q + 3] = kFp8 ? quad_scale<3>(kl) : kl;
             }
+            // (scaled unconditionally, then masked: a masked score is replaced whatever it holds)
+            float sc[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) sc[i] = S[i / 4][i % 4] * f[i];
             // This lane's row attends to tokens [lo, hs).  The common case takes one test per
             // pair: both blocks hold data throughout and every row sees all of the pair or none
             // of it.  Otherwise, per token, valid: it holds data this unit reads (V rows of other
@@ -1010,19 +1017,18 @@ struct MfmaSegment {
             const int hs = run_on ? min(rowL, last + 1) : lo;
             const bool fast = pr.ok[0] && pr.ok[1] && j16 >= lo && j16 + 2 * kBlockSize <= run_lv &&
                               !__ballot(hs > j16 && hs < j16 + 2 * kBlockSize);
-            float sc[8];
             bool valid[8], seen[8];
             if (fast) {
                 const bool on = hs > j16;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) sc[i] = on ? S[i / 4][i % 4] * f[i] : kNegInf;
+                for (int i = 0; i < 8; ++i) sc[i] = on ? sc[i] : kNegInf;
             } else {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const int t = j16 + kBlockSize * (i / 4) + 4 * g + i % 4;
                     valid[i] = pr.ok[i / 4] && t >= lo && t < run_lv;
                     seen[i] = valid[i] && run_on && t < rowL && t <= last;
-                    sc[i] = seen[i] ? S[i / 4][i % 4] * f[i] : kNegInf;
+                    sc[i] = seen[i] ? sc[i] : kNegInf;
                 }
             }
             // Pair maximum of head c over the four lane groups.  The reference m moves only
@@ -1038,12 +1044,11 @@ struct MfmaSegment {
             const float alpha = fast_exp2(m - ms);
             m = mn;
             float pw[8];
-            float psum = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                pw[i] = fast_exp2(sc[i] - ms);
-                psum += pw[i];
-            }
+            for (int i = 0; i < 8; ++i) pw[i] = fast_exp2(sc[i] - ms);
+            float psum = pw[0];
+#pragma unroll
+            for (int i = 1; i < 8; ++i) psum += pw[i];
             if constexpr (kFp8) {
 #pragma unroll
                 for (int q = 0; q < 2; ++q) {
@@ -1052,9 +1057,10 @@ struct MfmaSegment {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int i = 4 * q + r;
-                        // (unwritten slots may hold any scale, even NaN: only seen tokens are scaled)
-                        if (fast) pw[i] *= vsc[r];
-                        else pw[i] = seen[i] ? pw[i] * vsc[r] : 0.0f;
+                        // (unwritten slots may hold any scale, even NaN: the product of an unseen
+                        // token is replaced by zero)
+                        pw[i] *= vsc[r];
+                        if (!fast) pw[i] = seen[i] ? pw[i] : 0.0f;
                     }
                 }
             }
