@@ -19,10 +19,10 @@ constexpr int64_t kMaxWork = ((int64_t)1 << 30);  // waves, or (head group, bloc
 // Waves of the balanced split.  One wave per SIMD keeps the memory system saturated for
 // 16-bit caches (the matrix-core path streams two blocks per ring entry).  An FP8 block
 // carries half the bytes for about the same work per block, so FP8 caches run two waves
-// per SIMD, one wave's conversions and matrix products overlapping the other's loads;
-// shared-prefix groups stay at one wave per SIMD (twice the ranges would double their
-// 16-row partials and per-range start-up).  Workspace queries size for the larger count
-// (an upper bound).
+// per SIMD, one wave's conversions and matrix products overlapping the other's loads.
+// Shared-prefix groups stay at 1024 waves: their ranges are at least 16 positions long, so
+// more waves would leave teams idle and crowd the working ones onto half of the CUs.
+// Workspace queries size for the larger count (an upper bound).
 constexpr int64_t kBalancedWaves = 1024;       // 4 per CU
 constexpr int64_t kBalancedWavesFp8 = 2048;    // 8 per CU
 constexpr int32_t kMaxQueries = 4096;               // new tokens per sequence in one multi-query call

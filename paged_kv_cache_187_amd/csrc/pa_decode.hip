@@ -730,7 +730,7 @@ struct MfmaSegment {
             x23[u][1] = __builtin_amdgcn_perm(w[3][u], w[2][u], 0x07030602u);
         }
     }
-    // (a plain DPP move, which the compiler folds into the multiply that uses it)
+    // (a plain DPP move: one instruction, with no zeroed destination to set up first)
     template <int R>
     static __device__ __forceinline__ float quad_scale(float x) {
         return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), R * 0x55, 0xF, 0xF, true));
