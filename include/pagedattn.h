@@ -222,8 +222,8 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t nu
  * (num_seqs, num_heads, num_kv_heads, head_dim, max_context_len,
  * partition_size) the output is bitwise deterministic.
  *
- * Alignment: query, out, caches and workspace 16 bytes; block_tables and
- * context_lens 4 bytes; k_scale / v_scale (FP8 cache) 16 bytes.
+ * Alignment: query, out, caches and workspace 16 bytes; block_tables,
+ * context_lens and k_scale / v_scale (FP8 cache) 4 bytes.
  *
  * Supported (q_dtype, cache_dtype): (F16, F16), (BF16, BF16), (F16, FP8_E4M3),
  * (BF16, FP8_E4M3).  head_dim 64 or 128.  num_heads a multiple of

@@ -180,7 +180,7 @@ pa_status decode_impl(void* out, const void* query, const void* key_cache, const
     if (!aligned(out, 16) || !aligned(query, 16) || !aligned(key_cache, 16) || !aligned(value_cache, 16) ||
         !aligned(block_tables, 4) || !aligned(context_lens, 4) || (need > 0 && !aligned(workspace, 16)) ||
         (seq_group > 0 && !aligned(prefix_blocks, 4)) ||
-        (fp8 && (!aligned(k_scale, 16) || !aligned(v_scale, 16))))
+        (fp8 && (!aligned(k_scale, 4) || !aligned(v_scale, 4))))
         return PA_ERR_ALIGN;
     if (use_scratch && need > 0) {
         // every host check has passed: only now touch the device

@@ -162,6 +162,8 @@ def test_decode_host_checks(lib):
     assert _decode(lib, part=0) == WS                       # the balanced split always merges
     assert _decode(lib, out=FAKE + 2, ws=FAKE, wsb=1 << 30) == ALIGN
     assert _decode(lib, ws=FAKE + 4, wsb=1 << 30) == ALIGN
+    assert _decode(lib, cd=FP8, k_scale=FAKE + 2, v_scale=FAKE, ws=FAKE, wsb=1 << 30) == ALIGN   # scales: 4 bytes
+    assert _decode(lib, cd=FP8, k_scale=FAKE, v_scale=FAKE + 2, ws=FAKE, wsb=1 << 30) == ALIGN
     assert _decode(lib, B=0) == OK                          # nothing to do, nothing launched
 
 

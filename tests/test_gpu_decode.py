@@ -80,6 +80,29 @@ def test_fp8_cache_sweep(qd, D, hq, hkv, part):
     _run_and_check(cfg, what=f"fp8 D={D} G={hq // hkv} part={part}")
 
 
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (4, 4)])
+def test_fp8_scales_need_only_4_byte_alignment(hq, hkv):
+    """FP8 per-token scales at a 4-byte (not 16-byte) offset, on both decode paths (matrix cores
+    for G = 4, VALU for G = 1): the decode reads each scale with its own 4-byte load."""
+    _say(f"fp8 scales at a 4-byte offset Hq={hq} Hkv={hkv}")
+    cfg = _fp8cfg(num_heads=hq, num_kv_heads=hkv)
+    wh = synth.make_workload(cfg)
+    w = to_device(wh)
+    gpu_append(w)
+    shifted = []
+    for sc in (w.k_scale, w.v_scale):
+        buf = torch.empty(sc.numel() + 4, dtype=torch.float32, device=sc.device)
+        view = buf[1:1 + sc.numel()].view_as(sc)
+        view.copy_(sc)
+        assert view.data_ptr() % 16 == 4
+        shifted.append(view)
+    out = torch.empty_like(w.query)
+    pa.pa_decode(out, w.query, w.key_cache, w.value_cache, w.block_tables, w.context_lens, cfg.scale,
+                 w.max_context_len, partition_size=cfg.partition_size, k_scale=shifted[0], v_scale=shifted[1])
+    torch.cuda.synchronize()
+    assert_close(out, oracle_decode(wh, oracle_caches(wh)), cfg.cache_dtype, f"fp8 scales +4 bytes G={hq // hkv}")
+
+
 @pytest.mark.parametrize("qd,D,hq", [("bf16", 128, 1), ("bf16", 128, 4), ("f16", 128, 4), ("bf16", 64, 4),
                                      ("f16", 64, 8)])
 def test_fp8_every_code_through_single_token_contexts(qd, D, hq):
