@@ -635,7 +635,7 @@ def main():
                     help="override the workload's partition length (tokens; 0 = library's choice)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (this build has no "
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (the library has no "
               "multi-GPU path; the paged decode would shard by sequence or KV head with no exchange)",
               file=sys.stderr)
         sys.exit(2)
@@ -764,7 +764,7 @@ def main():
             "launch_us_p10_p50_p90_per_call_events": s["decode_us_p10_p50_p90_per_call_events"],
         },
         "also": also,
-        # achievable read bandwidth on this machine (probe kernels), labelled apart from the decode
+        # achievable read bandwidth on this GPU (probe kernels), labelled apart from the decode
         "ceiling": ceiling,
     }
     if oracle_pool is not None:

@@ -88,7 +88,7 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(const uint4* __restrict
     amax = wave_max[0];
     for (int w = 1; w < (int)(blockDim.x / kWave); ++w) amax = __builtin_fmaxf(amax, wave_max[w]);
 
-    // IEEE float32 division (correctly rounded: no fast-math in this build).
+    // IEEE float32 division (correctly rounded: the library is compiled without fast-math).
     const float scale = (amax == 0.0f) ? 1.0f : amax / 448.0f;
 
     for (int i = threadIdx.x; i < row_chunks; i += blockDim.x) {
