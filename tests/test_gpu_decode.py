@@ -234,6 +234,26 @@ def test_context_lens_clamped_to_the_stated_bounds(hq, hkv, part):
         assert torch.count_nonzero(out[3]) == 0
 
 
+@pytest.mark.parametrize("hq,hkv,cd", [(32, 32, "f16"), (32, 8, "fp8_e4m3"), (16, 2, "bf16")])
+def test_balanced_split_fewer_ranges_than_teams(hq, hkv, cd):
+    """A launch sized for 4096-token contexts over a few short sequences: the grid has all its
+    teams (1024 waves, 2048 for FP8; whole groups of eight workgroups, so the waves are
+    renumbered per XCD) but the lengths give only a handful of ranges, which go to evenly
+    spaced teams while the rest stay idle."""
+    _say(f"balanced: fewer ranges than teams Hq={hq} Hkv={hkv} cache={cd}")
+    lens = (1, 3, 17, 5, 0, 40)
+    cfg = _cfg(name="sparse", num_seqs=len(lens), num_heads=hq, num_kv_heads=hkv, len_args=lens,
+               q_dtype="f16" if cd == "f16" else "bf16", cache_dtype=cd, seed=31)
+    wh = synth.make_workload(cfg)
+    w = to_device(wh)
+    gpu_append(w)
+    out = torch.empty_like(w.query)
+    pa.pa_decode(out, w.query, w.key_cache, w.value_cache, w.block_tables, w.context_lens, cfg.scale, 4096,
+                 partition_size=0, k_scale=w.k_scale, v_scale=w.v_scale)
+    torch.cuda.synchronize()
+    assert_close(out, oracle_decode(wh, oracle_caches(wh)), cd, f"sparse ranges Hq={hq} Hkv={hkv}")
+
+
 def test_balanced_split_more_than_64_sequences():
     # 130 sequences (lengths walked 64 at a time), some empty, many ranges crossing sequences.
     _say("balanced: 130 sequences, empty ones")
