@@ -87,6 +87,15 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _dtype(t):
+    """The pa_dtype code of a tensor's element type (float16, bfloat16, or one-byte E4M3 codes)."""
+    code = _DTYPE.get(t.dtype)
+    if code is None:
+        raise ValueError(f"unsupported tensor dtype {t.dtype}: paged attention takes float16, bfloat16, "
+                         "or FP8 E4M3 codes as uint8 / float8_e4m3fn")
+    return code
+
+
 def _on_gpu(*tensors):
     for t in tensors:
         if t is None:
@@ -123,14 +132,14 @@ def pa_append_kv(key, value, key_cache, value_cache, slot_mapping, k_scale=None,
             value_cache.shape != key_cache.shape or slot_mapping.shape != (T,) or \
             slot_mapping.dtype != torch.int64:
         raise ValueError("inconsistent shapes for pa_append_kv")
-    cdt = _DTYPE[key_cache.dtype]
+    cdt = _dtype(key_cache)
     if cdt == PA_FP8_E4M3:
         for s in (k_scale, v_scale):
             if s is None or s.dtype != torch.float32 or s.shape != key_cache.shape[:2]:
                 raise ValueError("FP8 cache needs float32 k_scale / v_scale shaped [num_blocks, 16]")
     _check(load_library().pa_append_kv(
         _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache), _ptr(k_scale), _ptr(v_scale),
-        _ptr(slot_mapping), T, hkv, d, key_cache.shape[0], _DTYPE[key.dtype], cdt, _stream(stream)))
+        _ptr(slot_mapping), T, hkv, d, key_cache.shape[0], _dtype(key), cdt, _stream(stream)))
 
 
 def pa_copy_blocks(key_cache, value_cache, block_mapping, k_scale=None, v_scale=None, stream=None):
@@ -140,7 +149,7 @@ def pa_copy_blocks(key_cache, value_cache, block_mapping, k_scale=None, v_scale=
     if bs != BLOCK_SIZE or value_cache.shape != key_cache.shape or block_mapping.dtype != torch.int64 or \
             block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
         raise ValueError("inconsistent shapes for pa_copy_blocks")
-    cdt = _DTYPE[key_cache.dtype]
+    cdt = _dtype(key_cache)
     if cdt == PA_FP8_E4M3:
         for s in (k_scale, v_scale):
             if s is None or s.dtype != torch.float32 or s.shape != key_cache.shape[:2]:
@@ -164,7 +173,7 @@ def pa_swap_blocks(src, dst, block_mapping, stream=None):
             sk.shape[1] != BLOCK_SIZE or block_mapping.dtype != torch.int64 or block_mapping.dim() != 2 or \
             block_mapping.shape[1] != 2:
         raise ValueError("inconsistent shapes for pa_swap_blocks")
-    cdt = _DTYPE[sk.dtype]
+    cdt = _dtype(sk)
     _, _, hkv, d = sk.shape
     _check(load_library().pa_swap_blocks(
         _ptr(sk), _ptr(sv), _ptr(sks), _ptr(svs), sk.shape[0], _ptr(dk), _ptr(dv), _ptr(dks), _ptr(dvs),
@@ -224,7 +233,7 @@ def pa_decode_append(out, query, key_new, value_new, key_cache, value_cache, blo
     _check(load_library().pa_decode_append(
         _ptr(out), _ptr(query), _ptr(key_new), _ptr(value_new), _ptr(key_cache), _ptr(value_cache), _ptr(k_scale),
         _ptr(v_scale), _ptr(block_tables), _ptr(context_lens), B, hq, hkv, d, nb, block_tables.shape[1],
-        int(max_context_len), float(scale), int(partition_size), _DTYPE[query.dtype], _DTYPE[key_cache.dtype],
+        int(max_context_len), float(scale), int(partition_size), _dtype(query), _dtype(key_cache),
         _ptr(workspace), ws_bytes, _stream(stream)))
     return out
 
@@ -244,7 +253,7 @@ def pa_decode_noalloc(out, query, key_cache, value_cache, block_tables, context_
     _check(load_library().pa_decode_noalloc(
         _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(k_scale), _ptr(v_scale),
         _ptr(block_tables), _ptr(context_lens), B, hq, hkv, d, nb, block_tables.shape[1], int(max_context_len),
-        float(scale), int(partition_size), _DTYPE[query.dtype], _DTYPE[key_cache.dtype], _stream(stream)))
+        float(scale), int(partition_size), _dtype(query), _dtype(key_cache), _stream(stream)))
     return out
 
 
@@ -270,8 +279,8 @@ def _decode(window, out, query, key_cache, value_cache, block_tables, context_le
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = [_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(k_scale), _ptr(v_scale),
             _ptr(block_tables), _ptr(context_lens), B, hq, hkv, d, nb, block_tables.shape[1],
-            int(max_context_len), float(scale), int(partition_size), _DTYPE[query.dtype],
-            _DTYPE[key_cache.dtype], _ptr(workspace), ws_bytes, _stream(stream)]
+            int(max_context_len), float(scale), int(partition_size), _dtype(query),
+            _dtype(key_cache), _ptr(workspace), ws_bytes, _stream(stream)]
     lib = load_library()
     _check(lib.pa_decode(*args) if window is None else lib.pa_decode_sliding(*args, window))
     return out
@@ -301,7 +310,7 @@ def pa_decode_multi(out, query, key_cache, value_cache, block_tables, context_le
     _check(lib.pa_decode_multi(
         _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(k_scale), _ptr(v_scale),
         _ptr(block_tables), _ptr(context_lens), B, q_len, hq, hkv, d, nb, block_tables.shape[1],
-        int(max_context_len), float(scale), int(partition_size), _DTYPE[query.dtype], _DTYPE[key_cache.dtype],
+        int(max_context_len), float(scale), int(partition_size), _dtype(query), _dtype(key_cache),
         _ptr(workspace), ws_bytes, _stream(stream)))
     return out
 
@@ -334,7 +343,7 @@ def pa_decode_shared_prefix(out, query, key_cache, value_cache, block_tables, co
     _check(lib.pa_decode_shared_prefix(
         _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(k_scale), _ptr(v_scale),
         _ptr(block_tables), _ptr(context_lens), _ptr(prefix_blocks), int(group_size), B, hq, hkv, d, nb,
-        block_tables.shape[1], int(max_context_len), float(scale), _DTYPE[query.dtype], _DTYPE[key_cache.dtype],
+        block_tables.shape[1], int(max_context_len), float(scale), _dtype(query), _dtype(key_cache),
         _ptr(workspace), ws_bytes, _stream(stream)))
     return out
 

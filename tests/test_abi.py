@@ -309,3 +309,13 @@ def test_probe_library_exports_its_probes():
     lib.pa_probe_gather_teams.argtypes = [vp, vp, i32, i32, i32, i64, i32, vp, vp]
     assert lib.pa_probe_gather_teams(fake, fake, 16, 8, 128, 64, 2044, fake, None) != 0   # waves % heads
     assert lib.pa_probe_gather_teams(fake, fake, 16, 8, 64, 64, 2048, fake, None) != 0
+
+
+def test_binding_maps_dtypes_and_rejects_others():
+    import torch
+    from paged_kv_cache_187_amd import binding
+    assert binding._dtype(torch.zeros(1, dtype=torch.float16)) == F16
+    assert binding._dtype(torch.zeros(1, dtype=torch.bfloat16)) == BF16
+    assert binding._dtype(torch.zeros(1, dtype=torch.uint8)) == FP8
+    with pytest.raises(ValueError):
+        binding._dtype(torch.zeros(1, dtype=torch.float32))
