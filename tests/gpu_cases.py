@@ -81,10 +81,27 @@ def errors(out_gpu, ref):
     return max_abs, rel
 
 
+def worst_rows(out_gpu, ref):
+    """Diagnostics per output row (the leading indices: sequence, [query,] head): the row with the
+    largest max-abs error and the row with the largest relative L2 error, as text."""
+    if ref.ndim < 2 or ref.size == 0:
+        return ""
+    g = out_gpu.detach().to(torch.float64).cpu().numpy().reshape(ref.shape)
+    lead = ref.shape[:-1]
+    d = (g - ref).reshape(-1, ref.shape[-1])
+    r = ref.reshape(-1, ref.shape[-1])
+    row_abs = np.max(np.abs(d), axis=1)
+    norms = np.linalg.norm(r, axis=1)
+    row_rel = np.where(norms > 0, np.linalg.norm(d, axis=1) / np.where(norms > 0, norms, 1.0), 0.0)
+    ia, ir = int(np.argmax(row_abs)), int(np.argmax(row_rel))
+    at = lambda i: tuple(int(x) for x in np.unravel_index(i, lead))
+    return f" worst_abs_row={at(ia)}:{row_abs[ia]:.2e} worst_rel_row={at(ir)}:{row_rel[ir]:.2e}"
+
+
 def assert_close(out_gpu, ref, cache_dtype, what=""):
     max_abs, rel = errors(out_gpu, ref)
     tol_abs, tol_rel = TOL[cache_dtype]
-    print(f"[parity] {what} max_abs={max_abs:.3e} rel_l2={rel:.3e}", flush=True)
+    print(f"[parity] {what} max_abs={max_abs:.3e} rel_l2={rel:.3e}{worst_rows(out_gpu, ref)}", flush=True)
     assert max_abs <= tol_abs and rel <= tol_rel, f"{what}: max_abs={max_abs:.3e} rel_l2={rel:.3e}"
     return max_abs, rel
 
